@@ -1,0 +1,168 @@
+"""Throughput of the heterogeneous-adapter LoRA apply on one MI355X.
+
+Workload: Llama-7B decode BGMV -- 64 tokens (one per request), the q/k/v/o
+projections (4096 -> 4096) of one layer, 1000 rank-16 fp16 adapters scattered
+over a unified page pool.  A step applies every token's adapter to all four
+projections: y_i += s_a B_a (A_a x_i), shrink and expand fused in one launch
+(lora_bgmv_apply).  16 different id batches (with their own x and y buffers)
+rotate, so adapter pages come from HBM rather than the 256 MB Infinity Cache.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "BGMV/SGMV tokens/s and achieved HBM GB/s (% of peak), Llama-7B/70B shapes, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int) -> int:
+    """Bytes the method must move for one step: each distinct adapter's A and B
+    once per slice, x once, y read and written once."""
+    elt = 4 if wl.dtype == "f32" else 2
+    total = 0
+    uniq = sorted(set(int(a) for a in ids.tolist() if a >= 0))
+    n = len(ids)
+    for s in slices:
+        d_in, d_out = wl.slices[s]
+        for a in uniq:
+            total += int(wl.ranks[a]) * (d_in + d_out) * elt
+        total += n * d_in * elt + 2 * n * d_out * elt_y
+    return total
+
+
+def cpu_baseline(wl, batches, slices, threads: int):
+    import oracle
+    t0 = time.perf_counter()
+    ntok = 0
+    for b in batches:
+        for s in slices:
+            oracle.workload_reference(wl, b, s, n_threads=threads)
+        ntok += len(b.ids)
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full decode batches x %d slices (%d tokens), fp64 C oracle, %.2f s"
+                      % (len(batches), len(slices), ntok, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["fused", "split"], default="fused")
+    ap.add_argument("--batches", type=int, default=16)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this LoRA-apply path runs on a single GPU; --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gather_lora_matmul_amd as L
+    import workloads as W
+    from gather_lora_matmul_amd.synthetic import SyntheticPool, to_device
+
+    torch.cuda.set_device(0)
+    wl = W.make_workload(1)
+    slices = [0, 1, 2, 3]
+    print("[bench] building pool: %s, %d adapters x %d slices" % (wl.name, wl.n_adapters, len(slices)),
+          file=sys.stderr, flush=True)
+    sp = SyntheticPool(wl)
+    batches = [W.make_batch(wl, i) for i in range(args.batches)]
+    ids_d = [torch.from_numpy(b.ids).cuda() for b in batches]
+    xs = [[to_device(b.x[s], wl.dtype) for s in slices] for b in batches]
+    ys = [[to_device(b.y0[s], wl.dtype) for s in slices] for b in batches]
+    ydt = W.DTYPE_CODE[wl.dtype]
+    n = len(batches[0].ids)
+    v = [torch.zeros((n, sp.max_rank), dtype=torch.float32, device="cuda") for _ in slices]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        k = i % len(batches)
+        if args.mode == "fused":
+            L.lora_bgmv_apply(sp.handle, [(s, xs[k][j], ys[k][j]) for j, s in enumerate(slices)],
+                              ids_d[k], ydt, stream=stream)
+        else:
+            for j, s in enumerate(slices):
+                L.lora_bgmv_shrink(sp.handle, s, xs[k][j], ids_d[k], v[j], stream=stream)
+                L.lora_bgmv_expand(sp.handle, s, v[j], ids_d[k], ys[k][j], ydt, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: wall clock over exactly K steps, plus per-step HIP events on
+    # the launch stream for the kernel duration
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    toks = n * args.steps / wall
+    elt_y = 2
+    step_bytes = [algorithmic_bytes(wl, b.ids, slices, elt_y) for b in batches]
+    used = [step_bytes[(args.warmup + i) % len(batches)] for i in range(args.steps)]
+    avg_bytes = float(np.mean(used))
+    avg_kernel_s = float(np.mean(kern_ms)) * 1e-3
+    achieved = avg_bytes / avg_kernel_s / 1e9
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "bgmv_apply_llama7b_decode_traffic.json")
+    if os.path.exists(prof) and args.mode == "fused":
+        try:
+            with open(prof) as f:
+                tj = json.load(f)
+            traffic = tj.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+    out = {
+        "metric": METRIC,
+        "value": toks,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_decode_bgmv", "tokens_per_step": n,
+                   "slices": "q,k,v,o 4096x4096", "adapters": wl.n_adapters, "rank": 16,
+                   "weights": "fp16 N(0,0.02), pages scattered", "entry":
+                   "lora_bgmv_apply" if args.mode == "fused" else "lora_bgmv_shrink+expand",
+                   "id_batches_rotated": len(batches)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "kernel_us_per_step": float(np.mean(kern_ms)) * 1e3,
+        "algorithmic_MB_per_step": avg_bytes / 1e6,
+        "accumulate": "f32",
+    }
+    if not args.no_cpu:
+        threads = min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(wl, batches[:4], slices, threads)
+    sp.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

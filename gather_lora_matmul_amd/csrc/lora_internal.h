@@ -1,0 +1,105 @@
+// Internal declarations shared by the host runtime (pool, plan, entry points)
+// and the HIP kernels.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/lora_mi355x.h"
+
+namespace lora {
+
+// One (slice, adapter) row of the device adapter table: 32 bytes, read with a
+// single scalar load by every kernel.
+struct DevEntry {
+  int32_t rank;    // 0: adapter not resident in this slice
+  int32_t rs;      // stored B row length (rank rounded up to 16 bytes)
+  float scale;     // stored per-adapter scale
+  int32_t rpp;     // B rows per page = floor(P / rs)
+  int32_t a_off;   // index of the adapter's first A page id in the page-id list
+  int32_t b_off;   // index of its first B page id
+  float inv_rpp;   // 1.0f / rpp (quotient estimate, corrected exactly)
+  int32_t pad;
+};
+static_assert(sizeof(DevEntry) == 32, "DevEntry must stay 32 bytes");
+
+// Pool view handed to kernels.
+struct PoolView {
+  const char* pages;          // pool base
+  const DevEntry* entries;    // [n_slices][max_adapters]
+  const int32_t* page_ids;    // concatenated page lists
+  int32_t P;                  // elements per page
+  int32_t max_adapters;
+};
+
+// Per-slice input/output of one launch.
+struct IoDesc {
+  const void* x;
+  void* y;
+  int32_t slice;
+  int32_t d_in;
+  int32_t d_out;
+  int32_t npa;                // pages per A row = ceil(d_in / P)
+};
+
+struct IoSet {
+  IoDesc io[LORA_MAX_IO];
+  int32_t n_io;
+  int32_t max_d_out;
+  int32_t max_d_in;
+  int32_t pad;
+};
+
+// One unit of planned SGMV work: `count` tokens (perm[start .. start+count))
+// that all use `adapter` (-1: tokens with no adapter, only v rows are zeroed).
+struct PlanItem {
+  int32_t adapter;
+  int32_t start;
+  int32_t count;
+  int32_t kind;   // 0: VALU short item (count <= 4), 1: MFMA tile (count <= 64)
+};
+
+constexpr int kShortG = 4;   // tokens per short item
+constexpr int kTileM = 64;   // tokens per MFMA tile
+
+// ---- kernel launchers (defined in the .hip files) -------------------------
+hipError_t launch_fill_pages(char* pages, int64_t page_bytes, const int32_t* ids_dev,
+                             int64_t n, uint32_t pattern, int elt, hipStream_t s);
+hipError_t launch_fill_all(char* pages, int64_t bytes, uint32_t pattern, int elt,
+                           hipStream_t s);
+hipError_t launch_scatter_pages(char* pages, int64_t page_bytes, const char* staging,
+                                const int32_t* ids_dev, int64_t n, hipStream_t s);
+
+hipError_t launch_bgmv_shrink(int dtype, const PoolView& pv, const IoDesc& io,
+                              const int32_t* ids, int32_t n, float* v, int32_t v_ld,
+                              hipStream_t s);
+hipError_t launch_bgmv_expand(int dtype, int y_dtype, const PoolView& pv, const IoDesc& io,
+                              const float* v, int32_t v_ld, const int32_t* ids, int32_t n,
+                              const float* tok_scale, hipStream_t s);
+hipError_t launch_bgmv_apply(int dtype, int y_dtype, const PoolView& pv, const IoSet& ios,
+                             const int32_t* ids, int32_t n, hipStream_t s);
+
+struct PlanView {
+  const PlanItem* items;
+  const int32_t* perm;
+  int32_t n_items;
+  int32_t n_tokens;
+};
+
+hipError_t launch_sgmv_shrink(int dtype, const PoolView& pv, const PlanView& pl,
+                              const IoDesc& io, float* v, int32_t v_ld, hipStream_t s);
+hipError_t launch_sgmv_expand(int dtype, int y_dtype, const PoolView& pv, const PlanView& pl,
+                              const IoDesc& io, const float* v, int32_t v_ld, hipStream_t s);
+hipError_t launch_apply(int dtype, int y_dtype, const PoolView& pv, const PlanView& pl,
+                        const IoSet& ios, hipStream_t s);
+
+hipError_t launch_debug_resolve(const PoolView& pv, const IoDesc& io, int32_t max_rank,
+                                int elt, const int32_t* ids, int32_t n, int64_t* a_off,
+                                int64_t* b_off, hipStream_t s);
+hipError_t launch_debug_gather(int elt, const PoolView& pv, const IoDesc& io, int32_t adapter,
+                               int32_t rank, void* A, void* B, hipStream_t s);
+
+}  // namespace lora

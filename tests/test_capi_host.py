@@ -1,0 +1,230 @@
+"""Host-side checks of the C ABI (no GPU): exported symbols, pool layout and
+page-table contents on a host-only pool, allocator and planner invariants,
+error paths."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import gather_lora_matmul_amd as L
+import oracle
+import workloads as W
+from gather_lora_matmul_amd.synthetic import SyntheticPool
+
+
+def _declared_symbols():
+    import re
+    src = open(L.__file__.replace("gather_lora_matmul_amd/__init__.py", "include/lora_mi355x.h")).read()
+    return sorted(set(re.findall(r"^(?:lora_status|const char\*)\s+(lora_\w+)\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    decl = _declared_symbols()
+    assert len(decl) >= 20
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [s for s in decl if s not in exported]
+    assert not missing, missing
+    assert set(decl) == set(L.EXPORTS)
+    for s in decl:
+        assert getattr(L.lib(), s) is not None
+
+
+def test_library_has_gfx950_code_object():
+    # the offload bundle of the library built here names its target
+    with open(L.LIB_PATH, "rb") as f:
+        assert b"amdgcn-amd-amdhsa--gfx950" in f.read()
+
+
+def _host_pool(wl, **kw):
+    return SyntheticPool(wl, host_only=True, **kw)
+
+
+@pytest.mark.parametrize("cfg_args", [
+    ("f32", 256, 256, [4, 8, 8, 16], 256),          # the tiny configuration's shapes
+    ("bf16", 48, 40, [5, 3, 13], 32),              # d_in spans 2 pages, odd ranks, ragged B
+    ("f16", 64, 104, [16, 1, 9], 64),
+])
+def test_host_pool_layout_walks_back_to_dense(cfg_args):
+    dtype, d_in, d_out, ranks, P = cfg_args
+    wl = W.small_workload(dtype, d_in, d_out, ranks, P, n_slices=2)
+    with _host_pool(wl) as sp:
+        free, _ = L.lora_pool_info(sp.handle)
+        image = L.lora_pool_read_pages(sp.handle, 0, sp.n_pages, P, sp.dt)
+        seen = set()
+        for s in range(2):
+            for a in range(len(ranks)):
+                r, sc, ap, bp = L.lora_pool_export_entry(sp.handle, a, s)
+                assert r == ranks[a] and np.float32(sc) == wl.scales[a]
+                per16 = 16 // (4 if dtype == "f32" else 2)
+                rs = -(-r // per16) * per16
+                assert ap.size == r * -(-d_in // P) and bp.size == -(-d_out // (P // rs))
+                for pg in np.concatenate([ap, bp]).tolist():
+                    assert 0 <= pg < sp.n_pages and pg not in seen
+                    seen.add(pg)
+                A, B = oracle.walk_adapter(image, dtype, P, d_in, d_out, r, ap, bp)
+                A0, B0 = wl.weights(a, s)
+                assert A.tobytes() == A0.tobytes() and B.tobytes() == B0.tobytes()
+        assert free == sp.n_pages - len(seen)
+        # unused pages and page tails are NaN-poisoned
+        used = np.zeros(sp.n_pages, bool)
+        used[list(seen)] = True
+        pages = image.reshape(sp.n_pages, P)
+        nan_bits = W.NAN_BITS[dtype]
+        if dtype == "f32":
+            assert np.all(np.isnan(pages[~used]))
+        else:
+            assert np.all(pages[~used] == nan_bits)
+
+
+def test_pages_are_scattered_by_the_seed():
+    wl = W.small_workload("bf16", 64, 64, [8] * 6, 64)
+    with _host_pool(wl) as sp:
+        _, ap, _ = L.lora_pool_export_entry(sp.handle, 0, 0)[1:]
+        ap = L.lora_pool_export_entry(sp.handle, 0, 0)[2]
+    assert not np.all(np.diff(ap) == 1)
+
+
+def test_kv_dummy_pages_interleave():
+    wl = W.small_workload("bf16", 64, 64, [8] * 6, 64, kv_dummy_ratio=1.0)
+    with _host_pool(wl) as sp:
+        kv = np.concatenate(sp.kv_pages)
+        allp = []
+        for a in range(6):
+            _, _, ap, bp = L.lora_pool_export_entry(sp.handle, a, 0)
+            allp += ap.tolist() + bp.tolist()
+        assert len(set(kv.tolist()) & set(allp)) == 0
+        assert abs(len(kv) - len(allp)) <= 1
+
+
+def test_allocator_errors_leave_state_unchanged():
+    wl = W.small_workload("f16", 64, 64, [8, 8], 64)
+    sp = _host_pool(wl, n_pages=40)
+    h = sp.handle
+    free0, _ = L.lora_pool_info(h)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_alloc_pages(h, free0 + 1)
+    assert e.value.status == -2
+    assert L.lora_pool_info(h)[0] == free0
+    ids = L.lora_pool_alloc_pages(h, 3)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_free_pages(h, np.array([ids[0], ids[0]], np.int32))
+    assert e.value.status == -5
+    _, _, ap, _ = L.lora_pool_export_entry(h, 0, 0)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_free_pages(h, ap[:1])
+    assert e.value.status == -5
+    L.lora_pool_free_pages(h, ids)
+    assert L.lora_pool_info(h)[0] == free0
+    # double upload, rank out of range, eviction twice
+    A, B = wl.weights(0, 0)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_upload(h, 0, 0, 8, 1.0, A, B)
+    assert e.value.status == -5
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_upload(h, 1, 0, 9, 1.0, np.zeros((9, 64), np.uint16), np.zeros((64, 9), np.uint16))
+    assert e.value.status == -4
+    L.lora_pool_evict(h, 1, 0)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_evict(h, 1, 0)
+    assert e.value.status == -5
+    # not enough pages: NOMEM and nothing taken
+    big = np.zeros((8, 64), np.uint16)
+    free1 = L.lora_pool_info(h)[0]
+    L.lora_pool_alloc_pages(h, free1 - 3)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_upload(h, 1, 0, 8, 1.0, big, np.zeros((64, 8), np.uint16))
+    assert e.value.status == -2
+    assert L.lora_pool_info(h)[0] == 3
+    sp.close()
+
+
+def test_compute_refuses_host_only_and_stale_tables():
+    wl = W.small_workload("bf16", 64, 64, [8], 64)
+    with _host_pool(wl) as sp:
+        with pytest.raises(L.LoraError) as e:
+            L.lib().lora_bgmv_shrink  # exists
+            st = L.lib().lora_bgmv_shrink(sp.handle, 0, 16, 16, 1, 16, 8, None)
+            L._check(st, "bgmv_shrink")
+        assert e.value.status == -5
+
+
+def test_bad_pool_descriptions():
+    for kw, code in [(dict(page_elems=3), -1), (dict(max_rank=200), -4), (dict(max_rank=0), -4),
+                     (dict(n_pages=0), -1)]:
+        args = dict(page_elems=64, dtype=L.LORA_BF16, n_pages=16, max_adapters=2, max_rank=8,
+                    slice_dims=[(64, 64)], flags=L.LORA_POOL_HOST_ONLY)
+        args.update(kw)
+        with pytest.raises(L.LoraError) as e:
+            L.lora_pool_create(**args)
+        assert e.value.status == code, kw
+    with pytest.raises(L.LoraError):
+        L.lora_pool_create(64, L.LORA_BF16, 16, 2, 8, [(60, 64)], flags=L.LORA_POOL_HOST_ONLY)
+
+
+def _plan_for(wl, ids, l_long=0):
+    sp = _host_pool(wl)
+    plan = L.lora_plan_create(sp.handle, max(1, len(ids)))
+    L.lora_plan_build(plan, np.asarray(ids, np.int32), l_long=l_long, stream=0)
+    return sp, plan
+
+
+def test_planner_groups_the_index_vector_example():
+    # tokens 1..4 -> adapters #12, #05, #88, #12 (serving article, SGMV diagram)
+    wl = W.small_workload("bf16", 64, 64, [4] * 89, 64)
+    sp, plan = _plan_for(wl, [12, 5, 88, 12, -1])
+    perm, items = L.lora_plan_export(plan)
+    st = L.lora_plan_get_stats(plan)
+    assert st["n_groups"] == 4 and st["n_tokens"] == 5
+    groups = {}
+    for a, start, count, kind in items.tolist():
+        groups.setdefault(a, []).extend(perm[start:start + count].tolist())
+    assert groups == {12: [0, 3], 5: [1], 88: [2], -1: [4]}
+    L.lora_plan_destroy(plan)
+    sp.close()
+
+
+@pytest.mark.parametrize("l_long", [0, 1, 1 << 30])
+def test_planner_invariants(l_long):
+    rng = np.random.default_rng(7)
+    wl = W.small_workload("bf16", 64, 64, list(rng.choice([8, 16, 64, 40], 50)), 64)
+    ids = np.concatenate([np.full(150, 3), rng.integers(-1, 50, 400), np.full(70, 9)]).astype(np.int32)
+    rng.shuffle(ids)
+    sp, plan = _plan_for(wl, ids, l_long)
+    perm, items = L.lora_plan_export(plan)
+    assert sorted(perm.tolist()) == list(range(len(ids)))
+    covered = np.zeros(len(ids), int)
+    eff = 16 if l_long <= 0 else l_long
+    counts = {a: int(np.sum(ids == a)) for a in set(ids.tolist())}
+    for a, start, count, kind in items.tolist():
+        toks = perm[start:start + count]
+        covered[toks] += 1
+        assert np.all(ids[toks] == a) or (a == -1 and np.all(ids[toks] < 0))
+        assert np.all(np.diff(toks) > 0)           # stable: original order inside a group
+        if kind == 1:
+            assert a >= 0 and count <= 64 and counts[a] >= eff
+        else:
+            assert count <= 4 and (a < 0 or counts[a] < eff)
+    assert np.all(covered == 1)
+    kinds = items[:, 3]
+    assert np.all(np.diff(kinds) <= 0)              # MFMA tiles first
+    L.lora_plan_destroy(plan)
+    sp.close()
+
+
+def test_planner_rejects_bad_ids():
+    wl = W.small_workload("bf16", 64, 64, [8, 8], 64)
+    sp = _host_pool(wl, adapters=[0])
+    plan = L.lora_plan_create(sp.handle, 8)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_plan_build(plan, np.array([0, 1], np.int32), stream=0)
+    assert e.value.status == -3
+    with pytest.raises(L.LoraError) as e:
+        L.lora_plan_build(plan, np.array([0, 2], np.int32), stream=0)
+    assert e.value.status == -1
+    with pytest.raises(L.LoraError) as e:
+        L.lora_plan_build(plan, np.zeros(9, np.int32), stream=0)
+    assert e.value.status == -1
+    L.lora_plan_destroy(plan)
+    sp.close()

@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case prints its name, config and seed before it touches the GPU.  Inputs
+come from `workloads` (seeded); expected values only from `oracle`.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gather_lora_matmul_amd as L  # noqa: E402
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from gather_lora_matmul_amd.synthetic import SyntheticPool, from_device, to_device  # noqa: E402
+
+from gpu_helpers import Guarded, compare, exact_compare, ids_tensor, log, reference  # noqa: E402
+
+_POOLS = {}
+
+
+def pool_for(key, wl, adapters=None, **kw):
+    if key not in _POOLS:
+        log("[setup] pool %s (%s, %d adapters)" % (key, wl.name, wl.n_adapters if adapters is None
+                                                   else len(set(adapters))))
+        _POOLS[key] = SyntheticPool(wl, adapters=adapters, **kw)
+    return _POOLS[key]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cleanup():
+    yield
+    for p in _POOLS.values():
+        p.close()
+    _POOLS.clear()
+    torch.cuda.synchronize()
+
+
+def run_bgmv(sp, batch, slices, y_dtype, mode):
+    """mode: 'split' (shrink -> expand per slice) or 'fused' (one multi-slice apply)."""
+    wl = sp.wl
+    ids = ids_tensor(batch.ids)
+    n = len(batch.ids)
+    xs = {s: to_device(batch.x[s], wl.dtype) for s in slices}
+    ys = {s: Guarded(batch.y0[s], y_dtype) for s in slices}
+    ydt = W.DTYPE_CODE[y_dtype]
+    if mode == "split":
+        v_ld = sp.max_rank
+        for s in slices:
+            v = Guarded(np.full((n, v_ld), np.nan, np.float32), "f32")
+            L.lora_bgmv_shrink(sp.handle, s, xs[s], ids, v.view, v_ld)
+            L.lora_bgmv_expand(sp.handle, s, v.view, ids, ys[s].view, ydt, v_ld=v_ld)
+            v.host()
+    else:
+        L.lora_bgmv_apply(sp.handle, [(s, xs[s], ys[s].view) for s in slices], ids, ydt)
+    torch.cuda.synchronize()
+    return {s: ys[s].host() for s in slices}
+
+
+def run_sgmv(sp, batch, slices, y_dtype, mode, l_long=0):
+    wl = sp.wl
+    n = len(batch.ids)
+    plan = L.lora_plan_create(sp.handle, max(1, n))
+    L.lora_plan_build(plan, batch.ids, l_long=l_long)
+    xs = {s: to_device(batch.x[s], wl.dtype) for s in slices}
+    ys = {s: Guarded(batch.y0[s], y_dtype) for s in slices}
+    ydt = W.DTYPE_CODE[y_dtype]
+    if mode == "split":
+        v_ld = sp.max_rank
+        for s in slices:
+            v = Guarded(np.full((n, v_ld), np.nan, np.float32), "f32")
+            L.lora_sgmv_shrink(sp.handle, plan, s, xs[s], v.view, v_ld)
+            L.lora_sgmv_expand(sp.handle, plan, s, v.view, ys[s].view, ydt, v_ld=v_ld)
+            v.host()
+    else:
+        L.lora_apply(sp.handle, plan, [(s, xs[s], ys[s].view) for s in slices], ydt)
+    torch.cuda.synchronize()
+    stats = L.lora_plan_get_stats(plan)
+    L.lora_plan_destroy(plan)
+    return {s: ys[s].host() for s in slices}, stats
+
+
+# ---------------------------------------------------------------------------
+# page-table resolution and gather: bit exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [("f32", 256, 256, [4, 8, 8, 16], 256), ("bf16", 48, 40, [5, 3, 13], 32),
+                                   ("f16", 4096, 11008, [16, 64, 8], 4096)])
+def test_gather_and_resolve_bit_exact(shape):
+    dtype, d_in, d_out, ranks, P = shape
+    log("[case] gather/resolve %s" % (shape,))
+    wl = W.small_workload(dtype, d_in, d_out, ranks, P, n_slices=2, kv_dummy_ratio=1.0)
+    sp = SyntheticPool(wl)
+    try:
+        elt = 4 if dtype == "f32" else 2
+        sd = np.float32 if dtype == "f32" else np.uint16
+        for s in range(2):
+            for a in range(len(ranks)):
+                r = ranks[a]
+                A = torch.zeros((r, d_in), dtype=torch.int32 if elt == 4 else torch.int16, device="cuda")
+                B = torch.zeros((d_out, r), dtype=A.dtype, device="cuda")
+                L.lora_debug_gather(sp.handle, s, a, A, B)
+                torch.cuda.synchronize()
+                A0, B0 = wl.weights(a, s)
+                assert A.cpu().numpy().tobytes() == A0.tobytes()
+                assert B.cpu().numpy().tobytes() == B0.tobytes()
+            ids = np.array([2, -1, 0, 1, 1], np.int32) % len(ranks)
+            ids[1] = -1
+            npa = -(-d_in // P)
+            aoff = torch.zeros((len(ids), sp.max_rank * npa), dtype=torch.int64, device="cuda")
+            boff = torch.zeros((len(ids), d_out), dtype=torch.int64, device="cuda")
+            L.lora_debug_resolve(sp.handle, s, ids_tensor(ids), aoff, boff)
+            torch.cuda.synchronize()
+            aoff, boff = aoff.cpu().numpy(), boff.cpu().numpy()
+            for i, a in enumerate(ids.tolist()):
+                if a < 0:
+                    assert np.all(aoff[i] == -1) and np.all(boff[i] == -1)
+                    continue
+                r, _, ap, bp = L.lora_pool_export_entry(sp.handle, a, s)
+                per16 = 16 // elt
+                rs = -(-r // per16) * per16
+                rpp = P // rs
+                want_a = np.full(sp.max_rank * npa, -1, np.int64)
+                want_a[: r * npa] = ap.astype(np.int64) * P * elt
+                m = np.arange(d_out)
+                want_b = (bp[m // rpp].astype(np.int64) * P + (m % rpp) * rs) * elt
+                assert np.array_equal(aoff[i], want_a)
+                assert np.array_equal(boff[i], want_b)
+    finally:
+        sp.close()
+
+
+# ---------------------------------------------------------------------------
+# BGMV
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["split", "fused"])
+@pytest.mark.parametrize("ydt", ["own", "f32"])
+def test_bgmv_tiny(mode, ydt):
+    wl = W.make_workload(0)
+    y_dtype = wl.dtype if ydt == "own" else "f32"
+    log("[case] tiny bgmv mode=%s y=%s seed=%d" % (mode, y_dtype, wl.seed))
+    sp = pool_for("tiny", wl)
+    for bi in range(3):
+        b = W.make_batch(wl, bi, y_dtype=y_dtype, zero_y0=(bi != 2))
+        y = run_bgmv(sp, b, [0], y_dtype, mode)[0]
+        compare(y, reference(wl, b, 0, y_dtype), y_dtype, "tiny b%d" % bi)
+
+
+@pytest.mark.parametrize("mode", ["split", "fused"])
+def test_bgmv_llama7b_decode_full(mode):
+    wl = W.make_workload(1)
+    log("[case] llama7b decode bgmv full mode=%s" % mode)
+    sp = pool_for("cfg1", wl)
+    b = W.make_batch(wl, 0)
+    ys = run_bgmv(sp, b, [0, 1, 2, 3], wl.dtype, mode)
+    for s in range(4):
+        compare(ys[s], reference(wl, b, s, wl.dtype), wl.dtype, "cfg1 slice %d" % s)
+
+
+@pytest.mark.parametrize("mode", ["split", "fused"])
+def test_bgmv_hetero_decode_full(mode):
+    wl = W.make_workload(2)
+    log("[case] hetero decode bgmv full mode=%s" % mode)
+    sp = pool_for("cfg2", wl)
+    b = W.make_batch(wl, 0)
+    ys = run_bgmv(sp, b, [0, 1], wl.dtype, mode)
+    for s in range(2):
+        compare(ys[s], reference(wl, b, s, wl.dtype), wl.dtype, "cfg2 slice %d" % s)
+    # fp32 output: gate against the unrounded result
+    b32 = W.make_batch(wl, 1, y_dtype="f32")
+    ys = run_bgmv(sp, b32, [1], "f32", mode)
+    compare(ys[1], reference(wl, b32, 1, "f32"), "f32", "cfg2 slice 1 f32")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("mode", ["split", "fused"])
+def test_bgmv_exact_integer_bit_exact(cfg, mode):
+    wl = W.make_workload(cfg, exact=True)
+    b = W.make_batch(wl, 0, zero_y0=False)
+    used = sorted(set(b.ids.tolist()))
+    log("[case] exact bgmv cfg=%d mode=%s adapters=%d" % (cfg, mode, len(used)))
+    sp = pool_for(("exact", cfg), wl, adapters=used + list(range(0, wl.n_adapters, 97)))
+    ys = run_bgmv(sp, b, list(range(len(wl.slices))), wl.dtype, mode)
+    for s in range(len(wl.slices)):
+        exact_compare(ys[s], reference(wl, b, s, wl.dtype), wl.dtype, "exact cfg%d s%d" % (cfg, s))
+
+
+def test_bgmv_negative_ids_and_zero_scale():
+    wl = W.make_workload(2)
+    sp = pool_for("cfg2", wl)
+    b = W.make_batch(wl, 2, zero_y0=False, n_tokens=32)
+    b.ids[::3] = -1
+    log("[case] negative ids / zero token scale")
+    ys = run_bgmv(sp, b, [1], wl.dtype, "fused")
+    neg = b.ids < 0
+    assert ys[1][neg].tobytes() == b.y0[1][neg].tobytes()
+    compare(ys[1], reference(wl, b, 1, wl.dtype), wl.dtype, "neg ids")
+    # token scale override of 0 leaves y bit-identical
+    ids = ids_tensor(b.ids)
+    x = to_device(b.x[1], wl.dtype)
+    y = Guarded(b.y0[1], wl.dtype)
+    v = torch.zeros((32, sp.max_rank), dtype=torch.float32, device="cuda")
+    L.lora_bgmv_shrink(sp.handle, 1, x, ids, v)
+    L.lora_bgmv_expand(sp.handle, 1, v, ids, y.view, W.DTYPE_CODE[wl.dtype],
+                       token_scale=torch.zeros(32, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert y.host().tobytes() == b.y0[1].tobytes()
+    assert np.all(v.cpu().numpy()[neg] == 0)
+
+
+def test_bgmv_deterministic_and_placement_independent():
+    wl = W.make_workload(2)
+    b = W.make_batch(wl, 3, n_tokens=64)
+    used = sorted(set(b.ids.tolist()))
+    log("[case] determinism / shuffle invariance")
+    sp = pool_for("cfg2", wl)
+    y1 = run_bgmv(sp, b, [0, 1], wl.dtype, "fused")
+    y2 = run_bgmv(sp, b, [0, 1], wl.dtype, "fused")
+    wl2 = W.make_workload(2)
+    wl2.shuffle_seed = 99991
+    sp2 = SyntheticPool(wl2, adapters=used)
+    try:
+        y3 = run_bgmv(sp2, b, [0, 1], wl.dtype, "fused")
+    finally:
+        sp2.close()
+    for s in range(2):
+        assert y1[s].tobytes() == y2[s].tobytes()
+        assert y1[s].tobytes() == y3[s].tobytes()
+
+
+# ---------------------------------------------------------------------------
+# SGMV / fused apply
+# ---------------------------------------------------------------------------
+SMALL_SGMV = [
+    # dtype, d_in, d_out, ranks, P, ids
+    ("bf16", 256, 520, [16, 64, 5, 128], 256, [0] * 70 + [1] * 17 + [2] * 3 + [3] * 130 + [-1] * 5),
+    ("f16", 512, 264, [8, 40, 1], 256, [1] * 33 + [0, 2, 1, 0] * 9 + [2] * 16),
+    ("f32", 256, 256, [4, 8, 8, 16], 256, [0, 1, 2, 3] * 10 + [3] * 20),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_SGMV)))
+@pytest.mark.parametrize("mode", ["split", "fused"])
+@pytest.mark.parametrize("l_long", [0, 1 << 30])
+def test_sgmv_small(case, mode, l_long):
+    dtype, d_in, d_out, ranks, P, ids = SMALL_SGMV[case]
+    log("[case] sgmv small %d mode=%s l_long=%d" % (case, mode, l_long))
+    wl = W.small_workload(dtype, d_in, d_out, ranks, P, n_slices=2, seed=40 + case)
+    rng = np.random.default_rng(case)
+    ids = np.array(ids, np.int32)
+    rng.shuffle(ids)
+    b = W.custom_batch(wl, ids, zero_y0=True)
+    sp = pool_for(("small", case), wl)
+    ys, st = run_sgmv(sp, b, [0, 1], dtype, mode, l_long)
+    if dtype != "f32" and l_long == 0:
+        assert st["n_mfma_items"] > 0
+    for s in range(2):
+        compare(ys[s], reference(wl, b, s, dtype), dtype, "sgmv small %d s%d" % (case, s))
+
+
+@pytest.mark.parametrize("mode", ["split", "fused"])
+def test_sgmv_exact_small_bit_exact(mode):
+    wl = W.small_workload("bf16", 512, 328, [16, 64, 5, 128, 33], 256, n_slices=1, exact=True, seed=77)
+    ids = np.array([0] * 90 + [1] * 20 + [2] * 40 + [3] * 70 + [4] * 3 + [-1] * 4, np.int32)
+    np.random.default_rng(1).shuffle(ids)
+    b = W.custom_batch(wl, ids)
+    log("[case] sgmv exact small mode=%s" % mode)
+    sp = pool_for("exact_small", wl)
+    ys, st = run_sgmv(sp, b, [0], "bf16", mode)
+    assert st["n_mfma_items"] > 0
+    exact_compare(ys[0], reference(wl, b, 0, "bf16"), "bf16", "sgmv exact small")
+    y_b = run_bgmv(sp, b, [0], "bf16", "fused")[0]
+    assert y_b.tobytes() == ys[0].tobytes()
+
+
+def test_sgmv_llama13b_prefill_full():
+    wl = W.make_workload(3)
+    b = W.make_batch(wl, 0)
+    log("[case] llama13b prefill sgmv full, %d tokens" % len(b.ids))
+    sp = pool_for("cfg3", wl)
+    rng = np.random.default_rng(5)
+    sub = np.sort(rng.choice(len(b.ids), 192, replace=False))
+    for mode in ("split", "fused"):
+        ys, st = run_sgmv(sp, b, [0, 1], wl.dtype, mode)
+        assert st["n_mfma_items"] > 0
+        for s in range(2):
+            compare(ys[s][sub], reference(wl, b, s, wl.dtype, subset=sub), wl.dtype,
+                    "cfg3 %s s%d (sampled tokens)" % (mode, s))
+
+
+def test_mixed_llama70b_full():
+    wl = W.make_workload(4)
+    b = W.make_batch(wl, 0)
+    log("[case] llama70b mixed apply full, %d tokens" % len(b.ids))
+    sp = pool_for("cfg4", wl)
+    rng = np.random.default_rng(6)
+    sub = np.sort(np.concatenate([rng.choice(4096, 96, replace=False),
+                                  4096 + rng.choice(512, 64, replace=False)]))
+    ys, st = run_sgmv(sp, b, [0, 1], wl.dtype, "fused")
+    assert st["n_mfma_items"] > 0
+    for s in range(2):
+        compare(ys[s][sub], reference(wl, b, s, wl.dtype, subset=sub), wl.dtype,
+                "cfg4 fused s%d (sampled tokens)" % s)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_sgmv_exact_integer_config_shapes(cfg):
+    wl = W.make_workload(cfg, exact=True)
+    b = W.make_batch(wl, 0, zero_y0=False, n_tokens=1152 if cfg == 4 else 2048)
+    used = sorted(set(b.ids.tolist()))
+    log("[case] exact sgmv cfg=%d tokens=%d adapters=%d" % (cfg, len(b.ids), len(used)))
+    sp = pool_for(("exact", cfg), wl, adapters=used)
+    ys, st = run_sgmv(sp, b, [0, 1], wl.dtype, "fused")
+    rng = np.random.default_rng(cfg)
+    sub = np.sort(rng.choice(len(b.ids), 128, replace=False))
+    for s in range(2):
+        exact_compare(ys[s][sub], reference(wl, b, s, wl.dtype, subset=sub), wl.dtype,
+                      "exact cfg%d s%d" % (cfg, s))
+    ys2, _ = run_sgmv(sp, b, [0, 1], wl.dtype, "split")
+    for s in range(2):
+        assert ys2[s].tobytes() == ys[s].tobytes()
