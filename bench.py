@@ -103,19 +103,20 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: wall clock over exactly K steps, plus per-step HIP events on
-    # the launch stream for the kernel duration
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # timed region: wall clock over exactly K steps, bracketed by HIP events on
+    # the stream the kernels are launched on (average launch duration =
+    # event time / K; one launch per step in the fused mode)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         step(args.warmup + i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    kern_ms = np.array([e0.elapsed_time(e1) / args.steps])
     ms_per_step = wall * 1e3 / args.steps
     toks = n * args.steps / wall
     elt_y = 2

@@ -3,6 +3,8 @@
 // y_i += s_a B_a (A_a x_i) with a different adapter -- and possibly a different
 // rank -- per token, every adapter row gathered through the page table of the
 // unified pool (section "Unified Paging").
+#include <cstdlib>
+
 #include "kvalu.h"
 
 namespace lora {
@@ -63,9 +65,140 @@ __global__ __launch_bounds__(NT) void k_bgmv_expand(PoolView pv, IoDesc io,
 
 // ---- fused apply, several slices in one launch --------------------------------
 // Block = ((token, slice) unit, output-row split).  Each block computes the
-// whole shrink of its unit into LDS, then expands its row range.  The splits
-// of a unit share an XCD, so the repeated shrink reads hit that XCD's L2.
-template <typename T, typename TY, int NT, int U>
+// whole shrink of its unit into LDS, then expands its row range.  The first
+// pass of B rows (and y) is loaded before the shrink so both phases' loads are
+// in flight together.  The splits of a unit share an XCD, so the repeated
+// shrink reads hit that XCD's L2.  MAXN: largest B-row chunk count given a
+// prefetching body in this variant (bigger rows take the plain path).
+template <typename T, typename TY, int NT, int U, int NCH>
+__device__ __forceinline__ void bgmv_fused_body(const PoolView& pv, const DevEntry& e,
+                                                const IoDesc& io, int i, int m_lo, int m_hi,
+                                                float* part, float* vsh) {
+  const char* xr[1] = {reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * sizeof(T)};
+  char* yrow = reinterpret_cast<char*>(io.y) + (int64_t)i * io.d_out * sizeof(TY);
+  const float s = e.scale;
+  if constexpr (NCH > 0) {
+    ExpandPrefetch<T, TY, NT, NCH> pf;
+    const int m0 = m_lo + (int)threadIdx.x;
+    pf.load(pv, e, yrow, m0, m_hi);
+    valu_shrink<T, NT, U, 1, 16>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
+    pf.finish(vsh, s, yrow, m0, m_hi);
+    char* yr[1] = {yrow};
+    valu_expand<T, TY, NT, NCH, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo + NT * ExpandPrefetch<T, TY, NT, NCH>::RU,
+                                   m_hi);
+  } else {
+    valu_shrink<T, NT, U, 1, 16>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
+    char* yr[1] = {yrow};
+    valu_expand<T, TY, NT, 0, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo, m_hi);
+  }
+}
+
+// Fast body when A rows fit one page and one column pass covers d_in: every
+// page id is read first (B rows: one vector load per row; A rows: scalar
+// loads), then x, the first 16 A rows and the first pass of B rows and y are
+// all issued together, so a block waits for one dependent lookup and one data
+// round trip before its first arithmetic.
+template <typename T, typename TY, int NT, int U, int NCH>
+__device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEntry& e,
+                                                const IoDesc& io, int i, int m_lo, int m_hi,
+                                                float* part, float* vsh) {
+  constexpr int E = ET<T>::E;
+  constexpr int ELT = ET<T>::bytes;
+  constexpr int NW = NT / 64;
+  constexpr int KB = 16;
+  constexpr int RU = rows_per_pass(NCH);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int C = io.d_in / E;
+  const int r = e.rank;
+  const int mlast = m_hi - 1;
+  const char* xrow = reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * ELT;
+  char* yrow = reinterpret_cast<char*>(io.y) + (int64_t)i * io.d_out * sizeof(TY);
+  // (1) page ids: B rows (vector loads), the first 16 A rows (scalar loads);
+  //     indices are clamped, so every load below is unconditional
+  int64_t bo[RU];
+#pragma unroll
+  for (int ru = 0; ru < RU; ++ru) bo[ru] = b_offset(pv, e, ELT, min(m_lo + t + ru * NT, mlast));
+  int64_t ab[KB];
+#pragma unroll
+  for (int kk = 0; kk < KB; ++kk) ab[kk] = a_row_uniform(pv, e, ELT, min(kk, r - 1));
+  int cc[U];
+  bool cv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    cv[u] = t + NT * u < C;
+    cc[u] = cv[u] ? t + NT * u : C - 1;
+  }
+  // (2) all data of the first pass
+  uint4 xr[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) xr[u] = ld16(xrow + (int64_t)cc[u] * 16);
+  uint4 a[KB][U];
+#pragma unroll
+  for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[kk][u] = ld16(pv.pages + ab[kk] + (int64_t)cc[u] * 16);
+  uint4 b[RU][NCH];
+  float yv[RU];
+#pragma unroll
+  for (int ru = 0; ru < RU; ++ru) {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) b[ru][ch] = ld16(pv.pages + bo[ru] + ch * 16);
+    yv[ru] = load_y<TY>(yrow, min(m_lo + t + ru * NT, mlast));
+  }
+  // (3) shrink: first 16 rank rows, then the rest of the rank
+#pragma unroll
+  for (int u = 0; u < U; ++u) xr[u] = keep16(xr[u], cv[u]);
+#pragma unroll
+  for (int kk = 0; kk < KB; ++kk) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = dot16<T>(a[kk][u], xr[u], acc);
+    const float sum = wave_sum(acc);
+    if (lane == 0 && kk < r) part[w * kMaxR + kk] = sum;
+  }
+  for (int k0 = KB; k0 < r; k0 += KB) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) ab[kk] = a_row_uniform(pv, e, ELT, min(k0 + kk, r - 1));
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[kk][u] = ld16(pv.pages + ab[kk] + (int64_t)cc[u] * 16);
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      float acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc = dot16<T>(a[kk][u], xr[u], acc);
+      const float sum = wave_sum(acc);
+      if (lane == 0 && k0 + kk < r) part[w * kMaxR + k0 + kk] = sum;
+    }
+  }
+  __syncthreads();
+  for (int k = t; k < e.rs; k += NT) {
+    float sum = 0.f;
+    if (k < r) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) sum += part[ww * kMaxR + k];
+    }
+    vsh[k] = sum;
+  }
+  __syncthreads();
+  // (4) expand the prefetched rows, then any remaining ones
+  const float s = e.scale;
+#pragma unroll
+  for (int ru = 0; ru < RU; ++ru) {
+    const int m = m_lo + t + ru * NT;
+    float acc = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) acc = dot16v<T>(b[ru][ch], vsh + ch * E, acc);
+    if (m < m_hi) store_y<TY>(yrow, m, __builtin_fmaf(s, acc, yv[ru]));
+  }
+  char* yr[1] = {yrow};
+  valu_expand<T, TY, NT, NCH, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo + NT * RU, m_hi);
+}
+
+template <typename T, typename TY, int NT, int U, int MAXN>
 __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
                                                    const int32_t* __restrict__ ids, int n,
                                                    int nsplit, int rps) {
@@ -84,11 +217,23 @@ __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
   const int m_lo = q * rps;
   const int m_hi = min(io.d_out, m_lo + rps);
   if (m_lo >= m_hi) return;
-  const char* xr[1] = {reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * sizeof(T)};
-  valu_shrink<T, NT, U, 1, 16>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
-  char* yr[1] = {reinterpret_cast<char*>(io.y) + (int64_t)i * io.d_out * sizeof(TY)};
-  const float s = e.scale;
-  valu_expand_any<T, TY, NT, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo, m_hi);
+  const int nch = e.rs / ET<T>::E;
+  const bool fast = io.npa == 1 && io.d_in / ET<T>::E <= NT * U;
+#define LORA_FUSED_CASE(N)                                                                   \
+  if (N <= MAXN && nch == N) {                                                               \
+    if (fast)                                                                                \
+      bgmv_fused_fast<T, TY, NT, U, (N <= MAXN ? N : 1)>(pv, e, io, i, m_lo, m_hi, part, vsh); \
+    else                                                                                     \
+      bgmv_fused_body<T, TY, NT, U, (N <= MAXN ? N : 0)>(pv, e, io, i, m_lo, m_hi, part, vsh); \
+    return;                                                                                  \
+  }
+  LORA_FUSED_CASE(1)
+  LORA_FUSED_CASE(2)
+  LORA_FUSED_CASE(4)
+  LORA_FUSED_CASE(8)
+  LORA_FUSED_CASE(16)
+#undef LORA_FUSED_CASE
+  bgmv_fused_body<T, TY, NT, U, 0>(pv, e, io, i, m_lo, m_hi, part, vsh);
 }
 
 // ---- launchers ----------------------------------------------------------------
@@ -143,25 +288,51 @@ hipError_t expand_t(const PoolView& pv, const IoDesc& io, const float* v, int v_
   return hipGetLastError();
 }
 
+template <typename T, typename TY, int NT, int U>
+void apply_launch(const PoolView& pv, const IoSet& ios, const int32_t* ids, int n, dim3 grid,
+                  int nsplit, int rps, hipStream_t s) {
+  // variant by the pool's longest B row, so short-row pools get lean kernels
+  if (pv.max_nch <= 2)
+    hipLaunchKernelGGL((k_bgmv_apply<T, TY, NT, U, 2>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+  else if (pv.max_nch <= 4)
+    hipLaunchKernelGGL((k_bgmv_apply<T, TY, NT, U, 4>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+  else
+    hipLaunchKernelGGL((k_bgmv_apply<T, TY, NT, U, 8>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+}
+
+// Launch-shape overrides for tuning sweeps (0: automatic).
+inline int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+
 template <typename T, typename TY>
 hipError_t apply_t(const PoolView& pv, const IoSet& ios, const int32_t* ids, int n,
                    hipStream_t s) {
   constexpr int E = ET<T>::E;
   const int units = n * ios.n_io;
-  int nsplit, rps;
-  pick_split(units, ios.max_d_out, 2048, nsplit, rps);
+  static const int force_split = env_int("LORA_BGMV_SPLIT");
+  static const int force_nt = env_int("LORA_BGMV_NT");
+  // Splitting a unit repeats its whole shrink, which costs more than it
+  // gains (measured); split only when there are fewer units than CUs.
+  int nsplit = 1;
+  if (force_split > 0) {
+    nsplit = force_split;
+  } else {
+    while ((long)units * nsplit < 256 && ios.max_d_out / (nsplit * 2) >= 512) nsplit *= 2;
+  }
+  const int rps = (((ios.max_d_out + nsplit - 1) / nsplit) + 63) & ~63;
   const dim3 grid(xcd_grid(units, nsplit));
   const int C = ios.max_d_in / E;
-  if (C >= 512) {
+  if (force_nt == 256 && C <= 512) {
+    apply_launch<T, TY, 256, 2>(pv, ios, ids, n, grid, nsplit, rps, s);
+  } else if (C >= 512) {
     if (pick_u(ios.max_d_in, E, 512) == 1)
-      hipLaunchKernelGGL((k_bgmv_apply<T, TY, 512, 1>), grid, dim3(512), 0, s, pv, ios, ids, n,
-                         nsplit, rps);
+      apply_launch<T, TY, 512, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
     else
-      hipLaunchKernelGGL((k_bgmv_apply<T, TY, 512, 2>), grid, dim3(512), 0, s, pv, ios, ids, n,
-                         nsplit, rps);
+      apply_launch<T, TY, 512, 2>(pv, ios, ids, n, grid, nsplit, rps, s);
   } else {
-    hipLaunchKernelGGL((k_bgmv_apply<T, TY, 256, 1>), grid, dim3(256), 0, s, pv, ios, ids, n,
-                       nsplit, rps);
+    apply_launch<T, TY, 256, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
   }
   return hipGetLastError();
 }

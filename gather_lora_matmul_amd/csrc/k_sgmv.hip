@@ -1,13 +1,18 @@
 // Planned (SGMV) kernels: segments of tokens that share an adapter (multi-LoRA
-// serving article, SGMV section).  Short items (<= 4 tokens of one adapter) run
-// on the vector ALUs and read each adapter row once for all their tokens;
-// long groups run as 64-token bf16/fp16 MFMA tiles (kmfma.h).
+// serving article, SGMV section).  MFMA tiles (up to 64 tokens of one adapter,
+// kmfma.h) and short items (up to 4 tokens, vector ALUs, kvalu.h) are separate
+// kernel instantiations, each with its own register budget; a plan's items are
+// sorted MFMA tiles first, and each entry point launches one kernel per kind
+// present.
+#include <algorithm>
+
 #include "kmfma.h"
 #include "kvalu.h"
 
 namespace lora {
 
 constexpr int kSgNT = 256;
+constexpr int kShortLds = ((kSgNT / 64) * kShortG * kMaxR + kShortG * kMaxR) * 4;
 
 __device__ __forceinline__ void item_tokens(const PlanView& pl, const PlanItem& it,
                                             int (&tok)[kShortG]) {
@@ -20,21 +25,20 @@ __device__ __forceinline__ int split_rows(int d_out, int nsplit) {
 }
 
 // ---- shrink -------------------------------------------------------------------
-// Block = (item, group of rank rows).  v rows are indexed by original token.
+// Short items: block = (item, group of rank rows).  MFMA tiles: block = (tile,
+// 32-token half).  v rows are indexed by original token.
 template <typename T, int U>
-__global__ __launch_bounds__(kSgNT) void k_sgmv_shrink(PoolView pv, PlanView pl, IoDesc io,
-                                                       float* __restrict__ v, int v_ld,
-                                                       int ngroups, int rpg) {
-  __shared__ float part[(kSgNT / 64) * kShortG * kMaxR];
-  __shared__ float vsh[kShortG * kMaxR];
+__global__ __launch_bounds__(kSgNT) void k_sgmv_shrink_short(PoolView pv, PlanView pl, IoDesc io,
+                                                             float* __restrict__ v, int v_ld,
+                                                             int first, int count, int ngroups,
+                                                             int rpg) {
+  __shared__ __attribute__((aligned(16))) char lds[kShortLds];
+  float* part = reinterpret_cast<float*>(lds);
+  float* vsh = part + (kSgNT / 64) * kShortG * kMaxR;
   int it, grp;
   xcd_unit_split(blockIdx.x, ngroups, it, grp);
-  if (it >= pl.n_items) return;
-  const PlanItem item = pl.items[it];
-  if (item.kind == 1) {
-    if (grp == 0) mfma_shrink_tile<T, kSgNT>(pv, pl, item, io, v, v_ld);
-    return;
-  }
+  if (it >= count) return;
+  const PlanItem item = pl.items[first + it];
   int tok[kShortG];
   item_tokens(pl, item, tok);
   DevEntry e;
@@ -61,17 +65,29 @@ __global__ __launch_bounds__(kSgNT) void k_sgmv_shrink(PoolView pv, PlanView pl,
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kSgNT, 2) void k_sgmv_shrink_mfma(PoolView pv, PlanView pl, IoDesc io,
+                                                               float* __restrict__ v, int v_ld,
+                                                               int first, int count) {
+  __shared__ __attribute__((aligned(16))) char lds[kMfmaLds];
+  int it, half;
+  xcd_unit_split(blockIdx.x, 2, it, half);
+  if (it >= count) return;
+  const PlanItem item = pl.items[first + it];
+  mfma_shrink_tile<T>(pv, pl, item, io, half, v, v_ld, lds);
+}
+
 // ---- expand -------------------------------------------------------------------
 // Block = (item, range of output rows).
 template <typename T, typename TY>
-__global__ __launch_bounds__(kSgNT) void k_sgmv_expand(PoolView pv, PlanView pl, IoDesc io,
-                                                       const float* __restrict__ v, int v_ld,
-                                                       int nsplit) {
+__global__ __launch_bounds__(kSgNT, 2) void k_sgmv_expand_short(PoolView pv, PlanView pl, IoDesc io,
+                                                                const float* __restrict__ v, int v_ld,
+                                                                int first, int count, int nsplit) {
   __shared__ float vsh[kShortG * kMaxR];
   int it, q;
   xcd_unit_split(blockIdx.x, nsplit, it, q);
-  if (it >= pl.n_items) return;
-  const PlanItem item = pl.items[it];
+  if (it >= count) return;
+  const PlanItem item = pl.items[first + it];
   if (item.adapter < 0) return;
   const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
   if (e.rank <= 0) return;
@@ -79,10 +95,6 @@ __global__ __launch_bounds__(kSgNT) void k_sgmv_expand(PoolView pv, PlanView pl,
   const int m_lo = q * rps;
   const int m_hi = min(io.d_out, m_lo + rps);
   if (m_lo >= m_hi) return;
-  if (item.kind == 1) {
-    mfma_expand_tile<T, TY, kSgNT>(pv, pl, item, e, io, v, v_ld, m_lo, m_hi);
-    return;
-  }
   int tok[kShortG];
   item_tokens(pl, item, tok);
   for (int idx = threadIdx.x; idx < kShortG * e.rs; idx += kSgNT) {
@@ -101,19 +113,39 @@ __global__ __launch_bounds__(kSgNT) void k_sgmv_expand(PoolView pv, PlanView pl,
   valu_expand_any<T, TY, kSgNT, kShortG>(pv, e, vsh, kMaxR, sg, yr, m_lo, m_hi);
 }
 
+template <typename T, typename TY>
+__global__ __launch_bounds__(kSgNT, 2) void k_sgmv_expand_mfma(PoolView pv, PlanView pl, IoDesc io,
+                                                               const float* __restrict__ v, int v_ld,
+                                                               int first, int count, int nsplit) {
+  __shared__ __attribute__((aligned(16))) char lds[kMfmaLds];
+  int it, q;
+  xcd_unit_split(blockIdx.x, nsplit, it, q);
+  if (it >= count) return;
+  const PlanItem item = pl.items[first + it];
+  const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
+  if (e.rank <= 0) return;
+  const int rps = split_rows(io.d_out, nsplit);
+  const int m_lo = q * rps;
+  const int m_hi = min(io.d_out, m_lo + rps);
+  if (m_lo >= m_hi) return;
+  mfma_expand_tile<T, TY>(pv, pl, item, e, io, v, v_ld, m_lo, m_hi, lds);
+}
+
 // ---- fused apply ----------------------------------------------------------------
 // Block = ((item, slice) unit, output-row split).  The shrink result never leaves
-// the block: LDS for short items, LDS for MFMA tiles.
+// the block (LDS).
 template <typename T, typename TY, int U>
-__global__ __launch_bounds__(kSgNT) void k_apply(PoolView pv, PlanView pl, IoSet ios, int nsplit) {
-  __shared__ float part[(kSgNT / 64) * kShortG * kMaxR];
-  __shared__ float vsh[kShortG * kMaxR];
+__global__ __launch_bounds__(kSgNT, 2) void k_apply_short(PoolView pv, PlanView pl, IoSet ios,
+                                                          int first, int count, int nsplit) {
+  __shared__ __attribute__((aligned(16))) char lds[kShortLds];
+  float* part = reinterpret_cast<float*>(lds);
+  float* vsh = part + (kSgNT / 64) * kShortG * kMaxR;
   int unit, q;
   xcd_unit_split(blockIdx.x, nsplit, unit, q);
-  if (unit >= pl.n_items * ios.n_io) return;
+  if (unit >= count * ios.n_io) return;
   const int it = unit / ios.n_io;
   const int io_i = unit - it * ios.n_io;
-  const PlanItem item = pl.items[it];
+  const PlanItem item = pl.items[first + it];
   if (item.adapter < 0) return;
   const IoDesc io = ios.io[io_i];
   const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
@@ -122,10 +154,6 @@ __global__ __launch_bounds__(kSgNT) void k_apply(PoolView pv, PlanView pl, IoSet
   const int m_lo = q * rps;
   const int m_hi = min(io.d_out, m_lo + rps);
   if (m_lo >= m_hi) return;
-  if (item.kind == 1) {
-    mfma_apply_tile<T, TY, kSgNT>(pv, pl, item, e, io, m_lo, m_hi);
-    return;
-  }
   int tok[kShortG];
   item_tokens(pl, item, tok);
   const char* xr[kShortG];
@@ -141,51 +169,107 @@ __global__ __launch_bounds__(kSgNT) void k_apply(PoolView pv, PlanView pl, IoSet
   valu_expand_any<T, TY, kSgNT, kShortG>(pv, e, vsh, kMaxR, sg, yr, m_lo, m_hi);
 }
 
+template <typename T, typename TY>
+__global__ __launch_bounds__(kSgNT, 2) void k_apply_mfma(PoolView pv, PlanView pl, IoSet ios,
+                                                         int first, int count, int nsplit) {
+  __shared__ __attribute__((aligned(16))) char lds[kMfmaLds];
+  int unit, q;
+  xcd_unit_split(blockIdx.x, nsplit, unit, q);
+  if (unit >= count * ios.n_io) return;
+  const int it = unit / ios.n_io;
+  const int io_i = unit - it * ios.n_io;
+  const PlanItem item = pl.items[first + it];
+  const IoDesc io = ios.io[io_i];
+  const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
+  if (e.rank <= 0) return;
+  const int rps = split_rows(io.d_out, nsplit);
+  const int m_lo = q * rps;
+  const int m_hi = min(io.d_out, m_lo + rps);
+  if (m_lo >= m_hi) return;
+  mfma_apply_tile<T, TY>(pv, pl, item, e, io, m_lo, m_hi, lds);
+}
+
 // ---- launchers ------------------------------------------------------------------
 namespace {
 
 inline int sg_u(int d_in, int E) { return d_in / E > kSgNT ? 2 : 1; }
 
+// Output-row splits: grow until the grid reaches `target` blocks, keeping at
+// least `min_rows` rows per block.
+inline int pick_nsplit(int units, int d_out, int target, int min_rows) {
+  int nsplit = 1;
+  while ((long)units * nsplit < target && d_out / (nsplit * 2) >= min_rows) nsplit *= 2;
+  return nsplit;
+}
+
 template <typename T>
 hipError_t shrink_t(const PoolView& pv, const PlanView& pl, const IoDesc& io, float* v, int v_ld,
                     hipStream_t s) {
   constexpr int E = ET<T>::E;
-  int rpg = 16;
-  while (rpg > 4 && (long)pl.n_items * ((v_ld + rpg - 1) / rpg) < 512) rpg /= 2;
-  const int ngroups = (v_ld + rpg - 1) / rpg;
-  const dim3 grid(xcd_grid(pl.n_items, ngroups));
-  if (sg_u(io.d_in, E) == 1)
-    hipLaunchKernelGGL((k_sgmv_shrink<T, 1>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld, ngroups, rpg);
-  else
-    hipLaunchKernelGGL((k_sgmv_shrink<T, 2>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld, ngroups, rpg);
+  const int n_short = pl.n_items - pl.n_mfma;
+  if constexpr (ET<T>::bytes == 2) {
+    if (pl.n_mfma > 0)
+      hipLaunchKernelGGL((k_sgmv_shrink_mfma<T>), dim3(xcd_grid(pl.n_mfma, 2)), dim3(kSgNT), 0, s,
+                         pv, pl, io, v, v_ld, 0, pl.n_mfma);
+  }
+  if (n_short > 0) {
+    int rpg = 16;
+    while (rpg > 4 && (long)n_short * ((v_ld + rpg - 1) / rpg) < 512) rpg /= 2;
+    const int ngroups = (v_ld + rpg - 1) / rpg;
+    const dim3 grid(xcd_grid(n_short, ngroups));
+    if (sg_u(io.d_in, E) == 1)
+      hipLaunchKernelGGL((k_sgmv_shrink_short<T, 1>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld,
+                         pl.n_mfma, n_short, ngroups, rpg);
+    else
+      hipLaunchKernelGGL((k_sgmv_shrink_short<T, 2>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld,
+                         pl.n_mfma, n_short, ngroups, rpg);
+  }
   return hipGetLastError();
-}
-
-inline int pick_nsplit(int units, int d_out) {
-  int nsplit = 1;
-  while ((long)units * nsplit < 1024 && d_out / (nsplit * 2) >= 1024) nsplit *= 2;
-  return nsplit;
 }
 
 template <typename T, typename TY>
 hipError_t expand_t(const PoolView& pv, const PlanView& pl, const IoDesc& io, const float* v,
                     int v_ld, hipStream_t s) {
-  const int nsplit = pick_nsplit(pl.n_items, io.d_out);
-  const dim3 grid(xcd_grid(pl.n_items, nsplit));
-  hipLaunchKernelGGL((k_sgmv_expand<T, TY>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld, nsplit);
+  const int n_short = pl.n_items - pl.n_mfma;
+  if constexpr (ET<T>::bytes == 2) {
+    if (pl.n_mfma > 0) {
+      const int nsplit = pick_nsplit(pl.n_mfma, io.d_out, 512, 512);
+      hipLaunchKernelGGL((k_sgmv_expand_mfma<T, TY>), dim3(xcd_grid(pl.n_mfma, nsplit)), dim3(kSgNT),
+                         0, s, pv, pl, io, v, v_ld, 0, pl.n_mfma, nsplit);
+    }
+  }
+  if (n_short > 0) {
+    const int nsplit = pick_nsplit(n_short, io.d_out, 1024, 1024);
+    hipLaunchKernelGGL((k_sgmv_expand_short<T, TY>), dim3(xcd_grid(n_short, nsplit)), dim3(kSgNT), 0,
+                       s, pv, pl, io, v, v_ld, pl.n_mfma, n_short, nsplit);
+  }
   return hipGetLastError();
 }
 
 template <typename T, typename TY>
 hipError_t apply_t(const PoolView& pv, const PlanView& pl, const IoSet& ios, hipStream_t s) {
   constexpr int E = ET<T>::E;
-  const int units = pl.n_items * ios.n_io;
-  const int nsplit = pick_nsplit(units, ios.max_d_out);
-  const dim3 grid(xcd_grid(units, nsplit));
-  if (sg_u(ios.max_d_in, E) == 1)
-    hipLaunchKernelGGL((k_apply<T, TY, 1>), grid, dim3(kSgNT), 0, s, pv, pl, ios, nsplit);
-  else
-    hipLaunchKernelGGL((k_apply<T, TY, 2>), grid, dim3(kSgNT), 0, s, pv, pl, ios, nsplit);
+  const int n_short = pl.n_items - pl.n_mfma;
+  if constexpr (ET<T>::bytes == 2) {
+    if (pl.n_mfma > 0) {
+      // every split repeats the tile's shrink: split only until the grid
+      // covers the chip
+      const int nsplit = pick_nsplit(pl.n_mfma * ios.n_io, ios.max_d_out, 512, 2048);
+      hipLaunchKernelGGL((k_apply_mfma<T, TY>), dim3(xcd_grid(pl.n_mfma * ios.n_io, nsplit)),
+                         dim3(kSgNT), 0, s, pv, pl, ios, 0, pl.n_mfma, nsplit);
+    }
+  }
+  if (n_short > 0) {
+    const int units = n_short * ios.n_io;
+    const int nsplit = pick_nsplit(units, ios.max_d_out, 512, 2048);
+    const dim3 grid(xcd_grid(units, nsplit));
+    if (sg_u(ios.max_d_in, E) == 1)
+      hipLaunchKernelGGL((k_apply_short<T, TY, 1>), grid, dim3(kSgNT), 0, s, pv, pl, ios, pl.n_mfma,
+                         n_short, nsplit);
+    else
+      hipLaunchKernelGGL((k_apply_short<T, TY, 2>), grid, dim3(kSgNT), 0, s, pv, pl, ios, pl.n_mfma,
+                         n_short, nsplit);
+  }
   return hipGetLastError();
 }
 

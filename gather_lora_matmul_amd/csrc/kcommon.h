@@ -136,13 +136,49 @@ __device__ __forceinline__ void store_y<f16_t>(void* base, int64_t idx, float v)
   reinterpret_cast<uint16_t*>(base)[idx] = __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+// 16-bit storage <-> float without going through memory
+template <typename TY>
+__device__ __forceinline__ float bits_to_f(uint32_t h);
+template <>
+__device__ __forceinline__ float bits_to_f<bf16_t>(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+template <>
+__device__ __forceinline__ float bits_to_f<f16_t>(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+template <typename TY>
+__device__ __forceinline__ uint32_t f_to_bits(float f);
+template <>
+__device__ __forceinline__ uint32_t f_to_bits<bf16_t>(float f) {
+  return f32_to_bf16_rne(f);
+}
+template <>
+__device__ __forceinline__ uint32_t f_to_bits<f16_t>(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // ---- page-table resolution ---------------------------------------------------
+// Load of a wave-uniform index of a read-only table through the scalar cache:
+// the pointer is cast to the constant address space, so the load is an s_load
+// tracked by its own counter and never waits behind outstanding vector loads.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int idx) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  return ((cptr)p)[idx];
+}
+
 // Byte offset (from the pool base) of element j of A row k.
 __device__ __forceinline__ int64_t a_offset(const PoolView& pv, const DevEntry& e, int npa,
                                             int elt, int k, int j) {
   const int c = (npa == 1) ? 0 : j / pv.P;
   const int pg = pv.page_ids[e.a_off + k * npa + c];
   return ((int64_t)pg * pv.P + (j - c * pv.P)) * elt;
+}
+// Byte offset of the page holding A row k when a row fits one page (npa == 1);
+// k must be wave-uniform.
+__device__ __forceinline__ int64_t a_row_uniform(const PoolView& pv, const DevEntry& e, int elt,
+                                                 int k) {
+  return (int64_t)ld_uniform(pv.page_ids, e.a_off + k) * pv.P * elt;
 }
 // Byte offset of B row m (r_s elements, 16-byte aligned).
 __device__ __forceinline__ int64_t b_offset(const PoolView& pv, const DevEntry& e, int elt,
@@ -158,6 +194,23 @@ __device__ __forceinline__ int64_t b_offset(const PoolView& pv, const DevEntry& 
   }
   const int pg = pv.page_ids[e.b_off + q];
   return ((int64_t)pg * pv.P + (int64_t)rem * e.rs) * elt;
+}
+
+// Byte offset of B row m for a lane of a wave whose rows all lie in
+// [m0, m0 + 64), m0 wave-uniform: with rpp >= 64 those rows touch at most two
+// pages, whose ids are read with scalar loads (q_last bounds the page list).
+__device__ __forceinline__ int64_t b_offset_wave(const PoolView& pv, const DevEntry& e, int elt,
+                                                 int m, int m0, int q_last) {
+  int q0 = (int)((float)m0 * e.inv_rpp);
+  int rem0 = m0 - q0 * e.rpp;
+  if (rem0 < 0) --q0;
+  else if (rem0 >= e.rpp) ++q0;
+  const int pg0 = ld_uniform(pv.page_ids, e.b_off + q0);
+  const int pg1 = ld_uniform(pv.page_ids, e.b_off + min(q0 + 1, q_last));
+  int rem = m - q0 * e.rpp;
+  const bool second = rem >= e.rpp;
+  rem = second ? rem - e.rpp : rem;
+  return ((int64_t)(second ? pg1 : pg0) * pv.P + (int64_t)rem * e.rs) * elt;
 }
 
 // ---- wave reductions (DPP inside rows of 16, then 4 readlanes) --------------

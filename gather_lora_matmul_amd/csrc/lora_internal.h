@@ -33,6 +33,8 @@ struct PoolView {
   const int32_t* page_ids;    // concatenated page lists
   int32_t P;                  // elements per page
   int32_t max_adapters;
+  int32_t max_nch;            // 16-byte chunks in the longest stored B row of the pool
+  int32_t pad;
 };
 
 // Per-slice input/output of one launch.
@@ -82,11 +84,14 @@ hipError_t launch_bgmv_expand(int dtype, int y_dtype, const PoolView& pv, const 
 hipError_t launch_bgmv_apply(int dtype, int y_dtype, const PoolView& pv, const IoSet& ios,
                              const int32_t* ids, int32_t n, hipStream_t s);
 
+// Items [0, n_mfma) are MFMA tiles, [n_mfma, n_items) short items.
 struct PlanView {
   const PlanItem* items;
   const int32_t* perm;
   int32_t n_items;
   int32_t n_tokens;
+  int32_t n_mfma;
+  int32_t pad;
 };
 
 hipError_t launch_sgmv_shrink(int dtype, const PoolView& pv, const PlanView& pl,

@@ -4,9 +4,9 @@
 // segment of tokens sharing one adapter (multi-LoRA serving article, SGMV
 // section), whether its tokens were contiguous in the batch or not (the
 // article's index-vector diagram sends tokens 1 and 4 to the same adapter).
-// Groups long enough to be real dense contractions become 64-token MFMA tiles;
-// the rest become short items of up to four tokens that run on the vector
-// ALUs.  Items are ordered by rank band (rank rounded up to 16, the MFMA tile
+// Groups of at least l_long tokens (default 1: all of them, on 16-bit pools)
+// become MFMA tiles of up to 64 tokens; the rest, and every group of an fp32
+// pool, become short items of up to four tokens that run on the vector ALUs.  Items are ordered by rank band (rank rounded up to 16, the MFMA tile
 // width), largest first, so that the biggest items start first -- the "bands
 // of uniform granularity with little padding" of the article's FAQ on mixed
 // ranks.
@@ -65,7 +65,7 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
   if (!pl || (n > 0 && !ids) || n < 0) return fail(LORA_E_ARG, "bad argument");
   if (n > pl->max_tokens) return fail(LORA_E_ARG, "%d tokens exceed plan capacity %d", n, pl->max_tokens);
   lora_pool* p = pl->pool;
-  if (l_long <= 0) l_long = 16;
+  if (l_long <= 0) l_long = 1;  // 16-bit pools: every group runs on MFMA tiles
   const int NA = p->max_adapters;
   // validate and count (bucket NA holds the tokens without an adapter)
   std::vector<int32_t> count((size_t)NA + 1, 0);

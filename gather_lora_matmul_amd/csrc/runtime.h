@@ -79,6 +79,8 @@ struct lora_pool {
     v.page_ids = d_page_ids;
     v.P = P;
     v.max_adapters = max_adapters;
+    v.max_nch = rs_of(max_rank) * elt / 16;
+    v.pad = 0;
     return v;
   }
   lora::IoDesc io(int slice, const void* x, void* y) const {
@@ -101,7 +103,7 @@ struct lora_plan {
   int32_t n_items = 0;
   int32_t n_mfma = 0;
   int32_t mfma_tokens = 0;
-  int32_t l_long = 16;
+  int32_t l_long = 1;
   uint64_t pool_generation = ~0ull;
   bool built = false;
   std::vector<int32_t> h_perm;
@@ -118,6 +120,8 @@ struct lora_plan {
     v.perm = d_perm;
     v.n_items = n_items;
     v.n_tokens = n_tokens;
+    v.n_mfma = n_mfma;
+    v.pad = 0;
     return v;
   }
 };

@@ -186,12 +186,14 @@ typedef struct {
 lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** out);
 lora_status lora_plan_destroy(lora_plan* plan);
 /* Build the plan of one batch from host ids [n] (any order, -1 = no adapter):
- * stable counting sort by adapter -> groups; groups of at least l_long tokens
- * become 64-token MFMA tiles, the rest short items of <= 8 tokens; items ordered
- * by rank band, largest first.  l_long <= 0 selects the default (16).
- * Every id >= 0 must be < max_adapters and resident in every slice
- * (LORA_E_NOT_RESIDENT otherwise).  The plan is copied to the device on
- * `stream`; the host ids may be reused on return. */
+ * stable counting sort by adapter -> groups; on fp16/bf16 pools groups of at
+ * least l_long tokens become MFMA tiles of up to 64 tokens (l_long <= 0: 1, i.e.
+ * every group), the others -- and every group of an fp32 pool -- short items of
+ * <= 4 tokens on the vector ALUs; items ordered MFMA first, then by rank band,
+ * largest first.  Every id >= 0 must be < max_adapters and resident in every
+ * slice (LORA_E_NOT_RESIDENT otherwise).  The plan is copied to the device on
+ * `stream`; the host ids may be reused on return.  The SGMV calls below launch
+ * one kernel per item kind present in the plan. */
 lora_status lora_plan_build(lora_plan* plan, const int32_t* ids_host, int32_t n,
                             int32_t l_long, void* stream);
 lora_status lora_plan_get_stats(const lora_plan* plan, lora_plan_stats* out);

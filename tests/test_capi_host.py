@@ -195,7 +195,7 @@ def test_planner_invariants(l_long):
     perm, items = L.lora_plan_export(plan)
     assert sorted(perm.tolist()) == list(range(len(ids)))
     covered = np.zeros(len(ids), int)
-    eff = 16 if l_long <= 0 else l_long
+    eff = 1 if l_long <= 0 else l_long
     counts = {a: int(np.sum(ids == a)) for a in set(ids.tolist())}
     for a, start, count, kind in items.tolist():
         toks = perm[start:start + count]

@@ -243,7 +243,7 @@ SMALL_SGMV = [
 
 @pytest.mark.parametrize("case", range(len(SMALL_SGMV)))
 @pytest.mark.parametrize("mode", ["split", "fused"])
-@pytest.mark.parametrize("l_long", [0, 1 << 30])
+@pytest.mark.parametrize("l_long", [0, 16, 1 << 30])
 def test_sgmv_small(case, mode, l_long):
     dtype, d_in, d_out, ranks, P, ids = SMALL_SGMV[case]
     log("[case] sgmv small %d mode=%s l_long=%d" % (case, mode, l_long))
