@@ -41,6 +41,33 @@ def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int) -> int:
     return total
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources, so counter figures taken on other code are dropped."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gather_lora_matmul_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused decode kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None if the kernel sources
+    changed since the counters were taken."""
+    prof = os.path.join(ROOT, "profiles", "bgmv_apply_llama7b_decode_traffic.json")
+    try:
+        with open(prof) as f:
+            tj = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tj.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return tj.get("hbm_bytes_per_launch")
+
+
 def cpu_baseline(wl, batches, slices, threads: int):
     import oracle
     t0 = time.perf_counter()
@@ -63,6 +90,8 @@ def main():
     ap.add_argument("--mode", choices=["fused", "split"], default="fused")
     ap.add_argument("--batches", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 64 MiB device copy 10x (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this LoRA-apply path runs on a single GPU; --gpus %d is not supported"
@@ -125,15 +154,13 @@ def main():
     avg_bytes = float(np.mean(used))
     avg_kernel_s = float(np.mean(kern_ms)) * 1e-3
     achieved = avg_bytes / avg_kernel_s / 1e9
-    traffic = None
-    prof = os.path.join(ROOT, "profiles", "bgmv_apply_llama7b_decode_traffic.json")
-    if os.path.exists(prof) and args.mode == "fused":
-        try:
-            with open(prof) as f:
-                tj = json.load(f)
-            traffic = tj.get("hbm_bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic() if args.mode == "fused" else None
+    if args.copy_calib:
+        src = torch.empty(64 << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     out = {
         "metric": METRIC,
         "value": toks,
@@ -156,6 +183,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "kernel_us_per_step": float(np.mean(kern_ms)) * 1e3,
         "algorithmic_MB_per_step": avg_bytes / 1e6,
+        "kernel_source_hash": kernel_source_hash(),
         "accumulate": "f32",
     }
     if not args.no_cpu:
