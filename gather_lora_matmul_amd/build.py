@@ -1,6 +1,6 @@
 """Build liblora_mi355x.so (hipcc, gfx950) in-tree.
 
-    python -m gather_lora_matmul_amd.build      # or gather_lora_matmul_amd.build.build()
+    python gather_lora_matmul_amd/build.py      # (by path: importing the package loads the library)
 """
 from __future__ import annotations
 

@@ -125,6 +125,7 @@ lora_status lora_sgmv_shrink(lora_pool* p, const lora_plan* pl, int32_t slice, c
   if (!x || !v) return fail(LORA_E_ARG, "null device pointer");
   if (!aligned16(x)) return fail(LORA_E_ARG, "x not 16-byte aligned");
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
+  if (pl->n_mfma > 0) LORA_TRY(plan_reserve_part(const_cast<lora_plan*>(pl), 1));
   return hip_status(launch_sgmv_shrink(p->dtype, p->view(), pl->view(), p->io(slice, x, nullptr), v,
                                        v_ld, (hipStream_t)stream),
                     "sgmv_shrink");
@@ -155,6 +156,11 @@ lora_status lora_apply(lora_pool* p, const lora_plan* pl, int32_t n_io, const lo
   IoSet ios;
   LORA_TRY(build_ioset(p, n_io, io, ios));
   if (pl->n_tokens == 0) return LORA_OK;
+  lora_plan* mp = const_cast<lora_plan*>(pl);  // launch state: epoch and workspace
+  if (pl->n_mfma > 0) {
+    LORA_TRY(plan_reserve_part(mp, n_io));
+    if (++mp->epoch == 0) mp->epoch = 1;  // flags start at 0
+  }
   return hip_status(launch_apply(p->dtype, y_dtype, p->view(), pl->view(), ios, (hipStream_t)stream),
                     "apply");
 }

@@ -65,18 +65,6 @@ __global__ __launch_bounds__(kSgNT) void k_sgmv_shrink_short(PoolView pv, PlanVi
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kSgNT, 2) void k_sgmv_shrink_mfma(PoolView pv, PlanView pl, IoDesc io,
-                                                               float* __restrict__ v, int v_ld,
-                                                               int first, int count) {
-  __shared__ __attribute__((aligned(16))) char lds[kMfmaLds];
-  int it, half;
-  xcd_unit_split(blockIdx.x, 2, it, half);
-  if (it >= count) return;
-  const PlanItem item = pl.items[first + it];
-  mfma_shrink_tile<T>(pv, pl, item, io, half, v, v_ld, lds);
-}
-
 // ---- expand -------------------------------------------------------------------
 // Block = (item, range of output rows).
 template <typename T, typename TY>
@@ -111,24 +99,6 @@ __global__ __launch_bounds__(kSgNT, 2) void k_sgmv_expand_short(PoolView pv, Pla
     sg[g] = e.scale;
   }
   valu_expand_any<T, TY, kSgNT, kShortG>(pv, e, vsh, kMaxR, sg, yr, m_lo, m_hi);
-}
-
-template <typename T, typename TY>
-__global__ __launch_bounds__(kSgNT, 2) void k_sgmv_expand_mfma(PoolView pv, PlanView pl, IoDesc io,
-                                                               const float* __restrict__ v, int v_ld,
-                                                               int first, int count, int nsplit) {
-  __shared__ __attribute__((aligned(16))) char lds[kMfmaLds];
-  int it, q;
-  xcd_unit_split(blockIdx.x, nsplit, it, q);
-  if (it >= count) return;
-  const PlanItem item = pl.items[first + it];
-  const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
-  if (e.rank <= 0) return;
-  const int rps = split_rows(io.d_out, nsplit);
-  const int m_lo = q * rps;
-  const int m_hi = min(io.d_out, m_lo + rps);
-  if (m_lo >= m_hi) return;
-  mfma_expand_tile<T, TY>(pv, pl, item, e, io, v, v_ld, m_lo, m_hi, lds);
 }
 
 // ---- fused apply ----------------------------------------------------------------
@@ -169,24 +139,53 @@ __global__ __launch_bounds__(kSgNT, 2) void k_apply_short(PoolView pv, PlanView 
   valu_expand_any<T, TY, kSgNT, kShortG>(pv, e, vsh, kMaxR, sg, yr, m_lo, m_hi);
 }
 
+// ---- MFMA tiles: persistent kernels (one block range per block) -----------------
+template <typename T>
+__global__ __launch_bounds__(kMT, 2) void k_sgmv_shrink_tiles(PoolView pv, PlanView pl, IoDesc io,
+                                                              float* __restrict__ v, int v_ld) {
+  __shared__ __attribute__((aligned(16))) char misc[kMiscB];
+  __shared__ __attribute__((aligned(16))) char ba[kBufB];
+  __shared__ __attribute__((aligned(16))) char bb[kBufB];
+  __shared__ __attribute__((aligned(16))) char bc[kBufB];
+  const int L = logical_block(blockIdx.x, pl.G);
+  shrink_range<T>(pv, pl, io, 0, L, v, v_ld, LdsBufs{misc, ba, bb, bc});
+}
+
+// Split API: v rows of the tiles whose shrink several blocks shared (block = tile).
+__global__ __launch_bounds__(kMT) void k_sgmv_shrink_reduce(PoolView pv, PlanView pl, IoDesc io,
+                                                            float* __restrict__ v, int v_ld) {
+  __shared__ int toks[kTileM];
+  const int tile = blockIdx.x;
+  const PlanItem item = pl.items[tile];
+  const int rank = pv.entries[io.slice * pv.max_adapters + item.adapter].rank;
+  shrink_reduce_tile(pl, io, tile, rank, v, v_ld, toks);
+}
+
 template <typename T, typename TY>
-__global__ __launch_bounds__(kSgNT, 2) void k_apply_mfma(PoolView pv, PlanView pl, IoSet ios,
-                                                         int first, int count, int nsplit) {
-  __shared__ __attribute__((aligned(16))) char lds[kMfmaLds];
-  int unit, q;
-  xcd_unit_split(blockIdx.x, nsplit, unit, q);
-  if (unit >= count * ios.n_io) return;
-  const int it = unit / ios.n_io;
-  const int io_i = unit - it * ios.n_io;
-  const PlanItem item = pl.items[first + it];
-  const IoDesc io = ios.io[io_i];
-  const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
-  if (e.rank <= 0) return;
-  const int rps = split_rows(io.d_out, nsplit);
-  const int m_lo = q * rps;
-  const int m_hi = min(io.d_out, m_lo + rps);
-  if (m_lo >= m_hi) return;
-  mfma_apply_tile<T, TY>(pv, pl, item, e, io, m_lo, m_hi, lds);
+__global__ __launch_bounds__(kMT, 2) void k_sgmv_expand_tiles(PoolView pv, PlanView pl, IoDesc io,
+                                                              const float* __restrict__ v, int v_ld) {
+  __shared__ __attribute__((aligned(16))) char misc[kOffApg];
+  __shared__ __attribute__((aligned(16))) char ba[kVpB];
+  __shared__ __attribute__((aligned(16))) char bb[kVpB];
+  __shared__ __attribute__((aligned(16))) char bc[kDsB];
+  const int L = logical_block(blockIdx.x, pl.G);
+  expand_range<T, TY>(pv, pl, io, 0, L, v, v_ld, LdsBufs{misc, ba, bb, bc});
+}
+
+// Fused: every block first runs its shrink range of every slice (partial tiles,
+// each flagged with the launch epoch), then its expand range, waiting per tile
+// for its contributors' flags.  Launched cooperatively, so all G blocks are
+// resident and every wait ends.
+template <typename T, typename TY>
+__global__ __launch_bounds__(kMT, 2) void k_apply_tiles(PoolView pv, PlanView pl, IoSet ios) {
+  __shared__ __attribute__((aligned(16))) char misc[kMiscB];
+  __shared__ __attribute__((aligned(16))) char ba[kBufB];
+  __shared__ __attribute__((aligned(16))) char bb[kBufB];
+  __shared__ __attribute__((aligned(16))) char bc[kBufB];
+  const int L = logical_block(blockIdx.x, pl.G);
+  const LdsBufs lb{misc, ba, bb, bc};
+  for (int j = 0; j < ios.n_io; ++j) shrink_range<T>(pv, pl, ios.io[j], j, L, nullptr, 0, lb);
+  for (int j = 0; j < ios.n_io; ++j) expand_range<T, TY>(pv, pl, ios.io[j], j, L, nullptr, 0, lb);
 }
 
 // ---- launchers ------------------------------------------------------------------
@@ -202,15 +201,26 @@ inline int pick_nsplit(int units, int d_out, int target, int min_rows) {
   return nsplit;
 }
 
+// The fused tile kernel needs all G blocks resident at once.
+hipError_t cooperative_ok(const void* kernel, int G) {
+  int dev = 0, ncu = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kMT, 0);
+  if (e != hipSuccess) return e;
+  return (long)per_cu * ncu >= G ? hipSuccess : hipErrorCooperativeLaunchTooLarge;
+}
+
 template <typename T>
 hipError_t shrink_t(const PoolView& pv, const PlanView& pl, const IoDesc& io, float* v, int v_ld,
                     hipStream_t s) {
   constexpr int E = ET<T>::E;
   const int n_short = pl.n_items - pl.n_mfma;
   if constexpr (ET<T>::bytes == 2) {
-    if (pl.n_mfma > 0)
-      hipLaunchKernelGGL((k_sgmv_shrink_mfma<T>), dim3(xcd_grid(pl.n_mfma, 2)), dim3(kSgNT), 0, s,
-                         pv, pl, io, v, v_ld, 0, pl.n_mfma);
+    if (pl.n_mfma > 0) {
+      hipLaunchKernelGGL((k_sgmv_shrink_tiles<T>), dim3(pl.G), dim3(kMT), 0, s, pv, pl, io, v, v_ld);
+      hipLaunchKernelGGL(k_sgmv_shrink_reduce, dim3(pl.n_mfma), dim3(kMT), 0, s, pv, pl, io, v, v_ld);
+    }
   }
   if (n_short > 0) {
     int rpg = 16;
@@ -232,11 +242,9 @@ hipError_t expand_t(const PoolView& pv, const PlanView& pl, const IoDesc& io, co
                     int v_ld, hipStream_t s) {
   const int n_short = pl.n_items - pl.n_mfma;
   if constexpr (ET<T>::bytes == 2) {
-    if (pl.n_mfma > 0) {
-      const int nsplit = pick_nsplit(pl.n_mfma, io.d_out, 512, 512);
-      hipLaunchKernelGGL((k_sgmv_expand_mfma<T, TY>), dim3(xcd_grid(pl.n_mfma, nsplit)), dim3(kSgNT),
-                         0, s, pv, pl, io, v, v_ld, 0, pl.n_mfma, nsplit);
-    }
+    if (pl.n_mfma > 0)
+      hipLaunchKernelGGL((k_sgmv_expand_tiles<T, TY>), dim3(pl.G), dim3(kMT), 0, s, pv, pl, io, v,
+                         v_ld);
   }
   if (n_short > 0) {
     const int nsplit = pick_nsplit(n_short, io.d_out, 1024, 1024);
@@ -252,11 +260,14 @@ hipError_t apply_t(const PoolView& pv, const PlanView& pl, const IoSet& ios, hip
   const int n_short = pl.n_items - pl.n_mfma;
   if constexpr (ET<T>::bytes == 2) {
     if (pl.n_mfma > 0) {
-      // every split repeats the tile's shrink: split only until the grid
-      // covers the chip
-      const int nsplit = pick_nsplit(pl.n_mfma * ios.n_io, ios.max_d_out, 512, 2048);
-      hipLaunchKernelGGL((k_apply_mfma<T, TY>), dim3(xcd_grid(pl.n_mfma * ios.n_io, nsplit)),
-                         dim3(kSgNT), 0, s, pv, pl, ios, 0, pl.n_mfma, nsplit);
+      hipError_t e = cooperative_ok((const void*)k_apply_tiles<T, TY>, pl.G);
+      if (e != hipSuccess) return e;
+      PoolView a0 = pv;
+      PlanView a1 = pl;
+      IoSet a2 = ios;
+      void* args[] = {&a0, &a1, &a2};
+      e = hipLaunchCooperativeKernel((const void*)k_apply_tiles<T, TY>, dim3(pl.G), dim3(kMT), args, 0, s);
+      if (e != hipSuccess) return e;
     }
   }
   if (n_short > 0) {

@@ -1,28 +1,35 @@
 // MFMA tiles for groups of tokens that share one adapter (the long SGMV
 // segments of the multi-LoRA serving article, SGMV section).
 //
-// A tile is up to 64 token slots of one group, processed by one block of four
-// waves, with v_mfma_f32_16x16x32_{bf16,f16}.
+// A tile is up to 64 token slots of one group; blocks of four waves run
+// v_mfma_f32_16x16x32_{bf16,f16}.  The kernels are persistent: the planner
+// splits the tiles, weighted by the bytes they move, into one contiguous range
+// per block (BlockStart tables), so every block moves about the same number of
+// bytes and no block waits in a second round.
 //
-// Shrink  V[t][n] = sum_j X[t][j] A[n][j]         (M = tokens, N = rank, K = d_in)
-//   The four waves split K into quarters; each wave streams the X rows of all
-//   the tile's tokens and the A rows of its quarter straight from HBM into
-//   registers (double buffered, one 32-column step ahead), then the four
-//   partial tiles are summed in LDS in a fixed order.  N = rank padded to 16.
+// Shrink  V^T[n][t] = sum_j A[n][j] X[t][j]   (M = rank, N = tokens, K = d_in)
+//   Stages of 64 columns: the block loads the X rows of the tile's tokens and
+//   the A rows of the adapter with coalesced 16-byte loads (eight lanes per
+//   128-byte row segment) into registers two stages ahead, stores them to LDS
+//   and the waves read their MFMA operands from there; wave w owns tokens
+//   [16w, 16w + 16) and all rank blocks.  A block whose range covers only part
+//   of a tile's stages writes a partial tile; the block that completes the
+//   tile's stage count sums the partials in block order (deterministic).
 // Expand  Y^T[m][t] += s * sum_k B[m][k] V[t][k]  (M = output rows, N = tokens,
-//   K = rank).  B rows are read from their pages in natural [d_out][r_s] layout,
-//   which is exactly the MFMA A-operand layout (8 contiguous k per lane).  V is
-//   split into hi + lo 16-bit parts (packed in LDS) so that the fp32 shrink
-//   result enters the 16-bit MFMA with ~2^-16 relative error.  Each lane ends
-//   with 4 consecutive outputs of one token: one 8-byte read-modify-write of y.
-//   The waves take interleaved 16-row m-blocks, two per step, and load the next
-//   step's B rows and y before computing the current one.
+//   K = rank), in chunks of 64 rows: wave w computes rows [16w, 16w + 16) of
+//   the chunk for all tokens; B rows are read from their pages in natural
+//   [d_out][r_s] layout (the MFMA A-operand layout); V is split into hi + lo
+//   16-bit parts in LDS so the fp32 shrink result enters the 16-bit MFMA with
+//   ~2^-16 relative error.  The accumulators go through LDS so that y is read,
+//   updated and written with coalesced 16-byte accesses; y and B of the chunk
+//   two ahead are in flight while a chunk is computed.
 //
 // The same k-to-lane assignment is used for both operands of every MFMA, so the
 // hardware's internal k order does not matter; only the row/column placement
 // of the operands and of the accumulator (A row = lane % 16, B column =
 // lane % 16, accumulator column = lane % 16, rows 4 * (lane / 16) + i) is used.
-// All global loads are unconditional (clamped indices, masked values).
+// Global loads inside the pipelines are unconditional per lane (clamped
+// indices, masked values); only block-uniform conditions skip work.
 #pragma once
 
 #include "kcommon.h"
@@ -60,15 +67,6 @@ struct MfmaOp<f16_t> {
     lo = __builtin_bit_cast(uint16_t, (_Float16)(f - (float)h));
   }
 };
-template <>
-struct MfmaOp<float> {  // fp32 pools never form MFMA tiles (the planner keeps them short)
-  typedef bf16x8_t vec;
-  static __device__ __forceinline__ f32x4_t mma(const vec, const vec, const f32x4_t c) { return c; }
-  static __device__ __forceinline__ void split(float, uint16_t& hi, uint16_t& lo) { hi = lo = 0; }
-};
-
-constexpr int kVsStride = kMaxR + 4;          // LDS row stride of V (floats) = 528 bytes
-constexpr int kVsBytes = kTileM * kVsStride * 4;
 
 template <typename V>
 __device__ __forceinline__ V as_vec(const uint4 u) {
@@ -78,383 +76,627 @@ __device__ __forceinline__ uint4 keep16m(uint4 v, bool keep) {
   return keep ? v : make_uint4(0, 0, 0, 0);
 }
 
-// Token of every slot of the tile, -1 past the item's count (LDS).
+// ---- LDS layout -------------------------------------------------------------------
+// Four separate LDS arrays per block (separate arrays let the compiler see that
+// reading one buffer does not alias the global -> LDS loads in flight to the
+// others): `misc` (tile tokens, flags, A page ids) and three work buffers a, b,
+// c: the shrink's stage ring, or the expand's packed V (hi in a, lo in b) and
+// accumulator staging (c).
+constexpr int kMT = 256;                       // threads per block
+constexpr int kKC = 64;                        // shrink stage: columns of X and A
+constexpr int kRowB = kKC * 2;                 // staged row: 128 bytes (swizzled units)
+constexpr int kStageB = (kTileM + kMaxR) * kRowB;  // X rows, then A rows
+constexpr int kVpRow = kMaxR + 8;              // packed V half-row (uint16): hi or lo, pad
+constexpr int kDsRow = 64 + 4;                 // accumulator staging row (floats)
+constexpr int kOffToks = 0;                    // misc: int[64]
+constexpr int kOffMisc = 256;                  // misc: int[4]
+constexpr int kOffApg = 512;                   // misc: int[kMaxR][npa]: A page ids of the tile
+constexpr int kMiscB = kOffApg + kMaxR * kMaxNpa * 4;
+constexpr int kVpB = kTileM * kVpRow * 2;
+constexpr int kDsB = kTileM * kDsRow * 4;
+constexpr int kBufB = kStageB;
+static_assert(kVpB <= kBufB && kDsB <= kBufB, "expand buffers must fit the work buffers");
+static_assert(kMiscB + 3 * kBufB <= 80 * 1024, "two blocks per CU must fit the LDS");
+
+struct LdsBufs {
+  char* misc;
+  char* a;
+  char* b;
+  char* c;
+};
+
+// s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at
+// their maxima; vmcnt is split over bits 3:0 and 15:14).
+constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Block barrier for LDS traffic only: the wave's LDS accesses are complete
+// (lgkmcnt 0) and global loads in flight stay in flight.  __syncthreads also
+// waits for every outstanding global load of the wave, which would drain the
+// prefetch pipelines at every step.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));  // lgkmcnt(0) only
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// ---- block ranges -----------------------------------------------------------------
+struct Pos {
+  int tile;
+  int k;
+};
+__device__ __forceinline__ bool pos_lt(Pos a, int tile, int k) {
+  return a.tile < tile || (a.tile == tile && a.k < k);
+}
+// First unit (tile, stage or chunk) of logical block L in a slice whose tiles
+// have n units each.  L is block-uniform: the table entry is a scalar load.
+__device__ __forceinline__ Pos range_start(const BlockStart* bs, int L, int n, int n_tiles) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  const cptr p = (cptr)(bs + L);
+  const int tile = p[0], off = p[1], w = p[2];
+  if (tile >= n_tiles) return Pos{n_tiles, 0};
+  const int k = (int)(((uint32_t)n * (uint32_t)off + (uint32_t)w - 1u) / (uint32_t)w);  // n*off < 2^27
+  if (k >= n) return Pos{tile + 1, 0};
+  return Pos{tile, k};
+}
+// Blocks are dealt round-robin to the 8 XCDs; logical blocks [x*G/8, (x+1)*G/8)
+// run on XCD x, so neighbouring ranges (the same adapters) share an L2.
+__device__ __forceinline__ int logical_block(int b, int G) { return (b & 7) * (G >> 3) + (b >> 3); }
+
 __device__ __forceinline__ void load_tile_tokens(const PlanView& pl, const PlanItem& item,
                                                  int* toks) {
   if (threadIdx.x < kTileM)
     toks[threadIdx.x] = (int)threadIdx.x < item.count ? pl.perm[item.start + threadIdx.x] : -1;
 }
 
-// ---- shrink: V tile (fp32) into LDS Vs[slot][n], n < 16*NB ------------------
-// MBT: 16-token blocks in the tile (4 for 64 slots, 2 for 32 slots starting at
-// slot `slot0`).  Requires blockDim = 256 and toks[] visible to the block.
-template <typename T, int NB, int MBT>
-__device__ __forceinline__ void mfma_shrink_lds(const PoolView& pv, const DevEntry& e,
-                                                const IoDesc& io, const int* toks, int slot0,
-                                                float* Vs) {
+// ---- shrink ---------------------------------------------------------------------
+// One 16-byte global -> LDS load per lane: lane L's bytes land at lds + 16 L
+// (lds wave-uniform).  The data never passes through VGPRs.  Written as inline
+// asm so that the compiler does not track these LDS writes: it would otherwise
+// wait for every such load in flight before any LDS read it cannot prove
+// disjoint, draining the stage ring.  The callers wait for the loads
+// themselves (s_waitcnt vmcnt + barrier) before reading the stage; loads
+// return in order, so the compiler's own vmcnt waits stay correct (only more
+// conservative).  The asm has no register outputs.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la), "v"(g) : "memory", "m0");
+}
+
+// Staged rows are 128 bytes (64 columns) with the eight 16-byte units of row r
+// stored in the order u ^ (r & 7): the 16 rows an MFMA operand read touches
+// then fall on 16 different bank groups.
+__device__ __forceinline__ int stage_unit(int row, int u) { return row * 8 + (u ^ (row & 7)); }
+
+// acc[nb] (wave w, tokens [16w, 16w+16)) += the tile's stages [s0, s1).
+// A stage is X[64 slots][64 cols] and A[16*NB rank rows][64 cols], loaded into
+// one of two LDS buffers while the other is computed.
+template <typename T, int NB>
+__device__ __forceinline__ void shrink_stages(const PoolView& pv, const DevEntry& e,
+                                              const IoDesc& io, const int* toks, int count,
+                                              int s0, int s1, const LdsBufs& lb, f32x4_t (&acc)[NB]) {
   typedef typename MfmaOp<T>::vec vec;
-  constexpr int ELT = 2;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  constexpr int NAQ = (NB + 1) / 2;  // A loads per wave per stage (8 rows each)
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
+  const int ntb = (count + 15) >> 4;
   const int d_in = io.d_in;
-  const int r = e.rank;
-  // this lane's X rows (one per 16-token block) and A rows (one per 16-rank block)
-  const int tok0 = toks[slot0];
-  const char* xrow[MBT];
-  bool xok[MBT];
+  const int rank = e.rank;
+  // lane L of a load covers row 8 i + L / 8 of the load's 8 rows and the
+  // 16-byte unit that lands at position L % 8 of that row
+  const int lrow = lane >> 3;
+  const int c8 = 8 * ((lane & 7) ^ lrow);  // column within the stage
+  // X: load i = w + 4 q (q < 2) covers slots [8 i, 8 i + 8) (slots past the
+  // count repeat the last token: cache hits, never stored)
+  const char* xrow[2];
 #pragma unroll
-  for (int mb = 0; mb < MBT; ++mb) {
-    const int tk = toks[slot0 + mb * 16 + r16];
-    xok[mb] = tk >= 0;
-    xrow[mb] = reinterpret_cast<const char*>(io.x) + (int64_t)(tk >= 0 ? tk : tok0) * d_in * ELT;
+  for (int q = 0; q < 2; ++q) {
+    const int slot = 8 * (w + 4 * q) + lrow;
+    xrow[q] = reinterpret_cast<const char*>(io.x) + (int64_t)toks[min(slot, count - 1)] * d_in * 2;
   }
-  int64_t arow[NB];
-  bool aok[NB];
+  // A: load i = w + 4 q (q < NAQ) covers rank rows [8 i, 8 i + 8); rows past the
+  // rank repeat the last one (finite; no MFMA result column past the rank is kept)
+  const int* apg = reinterpret_cast<const int*>(lb.misc + kOffApg);
+  const int npa = io.npa;
+  const int P = pv.P;
+  const float invP = 1.0f / (float)P;
+  int arow[NAQ];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = nb * 16 + r16;
-    aok[nb] = n < r;
-    arow[nb] = io.npa == 1 ? a_offset(pv, e, 1, ELT, min(n, r - 1), 0) : 0;
-  }
-  // K split into four contiguous ranges of 32-column steps
-  const int nsteps = (d_in + 31) >> 5;
-  const int per = (nsteps + 3) >> 2;
-  const int s_beg = w * per;
-  const int s_end = min(nsteps, s_beg + per);
-  f32x4_t acc[MBT][NB];
+  for (int q = 0; q < NAQ; ++q) arow[q] = min(8 * (w + 4 * q) + lrow, rank - 1);
+  // Every wave issues the same 2 + NAQ loads per stage (none is skipped), so a
+  // wait with a fixed count separates the stages.
+  constexpr int LPS = 2 + NAQ;
+  auto issue = [&](int s, char* b) {
+    const int colc = min(kKC * s + c8, d_in - 8);
+    int c = (int)((float)colc * invP);  // page chunk: float quotient, corrected
+    int ofs = colc - c * P;
+    c = ofs < 0 ? c - 1 : (ofs >= P ? c + 1 : c);
+    ofs = colc - c * P;
 #pragma unroll
-  for (int mb = 0; mb < MBT; ++mb)
+    for (int q = 0; q < 2; ++q) load_lds16(xrow[q] + (int64_t)colc * 2, b + (w + 4 * q) * 1024);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 xc[MBT], ac[NB], xn[MBT], an[NB];
-  auto load_step = [&](int s, uint4 (&xo)[MBT], uint4 (&ao)[NB]) {
-    const int col = 32 * s + 8 * g;
-    const bool cok = col < d_in;
-    const int colc = cok ? col : d_in - 8;
-#pragma unroll
-    for (int mb = 0; mb < MBT; ++mb) xo[mb] = ld16(xrow[mb] + (int64_t)colc * ELT);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int64_t off = io.npa == 1 ? arow[nb] + (int64_t)colc * ELT
-                                      : a_offset(pv, e, io.npa, ELT, min(nb * 16 + r16, r - 1), colc);
-      ao[nb] = ld16(pv.pages + off);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MBT; ++mb) xo[mb] = keep16m(xo[mb], cok && xok[mb]);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) ao[nb] = keep16m(ao[nb], cok && aok[nb]);
+    for (int q = 0; q < NAQ; ++q)
+      load_lds16(pv.pages + ((int64_t)apg[arow[q] * npa + c] * P + ofs) * 2,
+                 b + kTileM * kRowB + (w + 4 * q) * 1024);
   };
-  if (s_beg < s_end) {
-    // double buffered while the registers allow (ranks up to 64)
-    constexpr bool kDouble = NB <= 4;
-    load_step(s_beg, xc, ac);
-    for (int s = s_beg; s < s_end; ++s) {
-      if constexpr (kDouble) load_step(min(s + 1, s_end - 1), xn, an);  // next step in flight
+  auto compute = [&](int s, const char* b) {
+    if (w < ntb) {
+      const int row = 16 * w + r16;
 #pragma unroll
-      for (int mb = 0; mb < MBT; ++mb)
+      for (int ks = 0; ks < 2; ++ks) {
+        // X columns past d_in (last stage only) are zero; A there is finite
+        const bool cok = kKC * s + 32 * ks + 8 * g < d_in;
+        const uint4 xo = keep16m(*reinterpret_cast<const uint4*>(b + 16 * stage_unit(row, 4 * ks + g)), cok);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = MfmaOp<T>::mma(as_vec<vec>(xc[mb]), as_vec<vec>(ac[nb]), acc[mb][nb]);
-      if constexpr (kDouble) {
-#pragma unroll
-        for (int mb = 0; mb < MBT; ++mb) xc[mb] = xn[mb];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) ac[nb] = an[nb];
-      } else if (s + 1 < s_end) {
-        load_step(s + 1, xc, ac);
+        for (int nb = 0; nb < NB; ++nb) {
+          const int ar = 16 * nb + r16;
+          const uint4 ao =
+              *reinterpret_cast<const uint4*>(b + kTileM * kRowB + 16 * stage_unit(ar, 4 * ks + g));
+          acc[nb] = MfmaOp<T>::mma(as_vec<vec>(ao), as_vec<vec>(xo), acc[nb]);
+        }
       }
     }
+  };
+  // Three-buffer ring: stages s + 1 and s + 2 are in flight while stage s is
+  // computed.  Each step waits for the wave's own loads of stage s (the two
+  // later stages stay outstanding); the barrier then makes every wave's loads
+  // of stage s visible and frees the buffer of stage s - 1 for stage s + 2.
+  // Past s1 - 1 the issues repeat the last stage (never computed).
+  auto step = [&](int s, const char* cur, char* nxt2) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(LPS));
+    lds_barrier();
+    issue(min(s + 2, s1 - 1), nxt2);
+    compute(s, cur);
+  };
+  issue(s0, lb.a);
+  issue(min(s0 + 1, s1 - 1), lb.b);
+  for (int s = s0; s < s1; s += 3) {
+    step(s, lb.a, lb.c);
+    if (s + 1 < s1) step(s + 1, lb.b, lb.a);
+    if (s + 2 < s1) step(s + 2, lb.c, lb.b);
   }
-  // fixed-order sum of the four partial tiles: wave 0 stores, waves 1..3 add
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no load may land after the range
+  __syncthreads();
+}
+
+// ---- shrink outputs ---------------------------------------------------------------
+// A block's contribution to a tile is a partial tile in the MFMA lane layout:
+// float4 unit (nb * ntb + w) * 64 + lane holds ranks 16 nb + 4 g + [0, 4) of
+// slot 16 w + r16 (ntb = token blocks of the tile).  Contribution c of a tile
+// (its entry in the slice's list) sits at its listed offset in the launch
+// slice's region.
+__device__ __forceinline__ const int32_t* contrib_list(const PlanView& pl, int slice) {
+  return pl.contrib + (int64_t)slice * 2 * pl.contrib_cap;
+}
+__device__ __forceinline__ float4* part_at(const PlanView& pl, int j, int32_t off) {
+  return reinterpret_cast<float4*>(pl.part) + (int64_t)j * pl.part_stride + off;
+}
+// Unit u of a partial tile with ntb token blocks -> (slot, first rank)
+__device__ __forceinline__ int unit_slot(int u, int ntb) { return 16 * ((u >> 6) % ntb) + (u & 15); }
+__device__ __forceinline__ int unit_rank(int u, int ntb) { return 16 * ((u >> 6) / ntb) + 4 * ((u & 63) >> 4); }
+
+// v[token][n .. n + 4) of a tile slot (split API rows; n >= rank -> 0).
+__device__ __forceinline__ void v_store4(float* v, int v_ld, int tok, int n, int rank, float4 a4) {
+  float* row = v + (int64_t)tok * v_ld;
+  const float a[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-      for (int mb = 0; mb < MBT; ++mb)
+  for (int i = 0; i < 4; ++i)
+    if (n + i < v_ld) row[n + i] = n + i < rank ? a[i] : 0.f;
+}
+// v columns [w0, v_ld) of the tile's tokens are zero.
+__device__ __forceinline__ void v_zero_tail(float* v, int v_ld, const int* toks, int count, int w0) {
+  const int nz = v_ld - w0;
+  if (nz <= 0) return;
+  for (int idx = threadIdx.x; idx < count * nz; idx += kMT) {
+    const int slot = idx / nz;
+    v[(int64_t)toks[slot] * v_ld + w0 + (idx - slot * nz)] = 0.f;
+  }
+}
+
+// One tile of the block's shrink range: stages [k0, k1) of nst.  Split API
+// (v != null): a block that covers the whole tile writes v; others write their
+// partial tile, summed by the reduce kernel.  Fused (v == null): every
+// contribution is a partial tile, flagged with the launch epoch once written.
+template <typename T, int NB>
+__device__ __forceinline__ void shrink_tile(const PoolView& pv, const PlanView& pl,
+                                            const DevEntry& e, const IoDesc& io, int j, int L,
+                                            int tile, int count, int k0, int k1, int nst,
+                                            bool first_of_range, float* v, int v_ld,
+                                            const LdsBufs& lb) {
+  const int* toks = reinterpret_cast<const int*>(lb.misc + kOffToks);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int ntb = (count + 15) >> 4;
+  f32x4_t acc[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  shrink_stages<T, NB>(pv, e, io, toks, count, k0, k1, lb, acc);
+  const int slot = 16 * w + r16;
+  if (v && k0 == 0 && k1 == nst) {
+    if (w < ntb && slot < count) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* p = Vs + (slot0 + mb * 16 + 4 * g + i) * kVsStride + nb * 16 + r16;
-            *p = ww == 0 ? acc[mb][nb][i] : *p + acc[mb][nb][i];
+      for (int nb = 0; nb < NB; ++nb)
+        v_store4(v, v_ld, toks[slot], 16 * nb + 4 * g, e.rank,
+                 make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]));
+    }
+    v_zero_tail(v, v_ld, toks, count, 16 * NB);
+  } else {
+    // this contribution's entry in the tile's list (block-uniform scalar loads)
+    const int entry = (L << 1) | (first_of_range ? 0 : 1);
+    const int32_t* lst = contrib_list(pl, io.slice);
+    const int32_t* off = pl.contrib_off + io.slice * (pl.tile_cap + 1);
+    int c = off[tile];
+    while (c < off[tile + 1] - 1 && lst[2 * c] != entry) ++c;
+    float4* part = part_at(pl, j, lst[2 * c + 1]);
+    if (w < ntb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        part[(nb * ntb + w) * 64 + lane] = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+    }
+    if (!v) {
+      __syncthreads();  // the block's partial stores are done
+      if (t == 0)
+        __hip_atomic_store(pl.flags + j * pl.contrib_cap + c, pl.epoch, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
+
+// The block's shrink range in launch slice j.
+template <typename T>
+__device__ __forceinline__ void shrink_range(const PoolView& pv, const PlanView& pl,
+                                             const IoDesc& io, int j, int L, float* v, int v_ld,
+                                             const LdsBufs& lb) {
+  const int nst = (io.d_in + kKC - 1) / kKC;
+  const Pos a = range_start(pl.bs_shrink, L, nst, pl.n_mfma);
+  const Pos b = range_start(pl.bs_shrink, L + 1, nst, pl.n_mfma);
+  int* toks = reinterpret_cast<int*>(lb.misc + kOffToks);
+  for (int i = a.tile; i < pl.n_mfma && pos_lt(Pos{i, 0}, b.tile, b.k); ++i) {
+    const int k0 = i == a.tile ? a.k : 0;
+    const int k1 = i == b.tile ? b.k : nst;
+    if (k0 >= k1) continue;
+    const PlanItem item = pl.items[i];
+    const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
+    load_tile_tokens(pl, item, toks);
+    {  // A page ids of the tile's rank rows (rows past the rank repeat the last)
+      int* apg = reinterpret_cast<int*>(lb.misc + kOffApg);
+      const int rp = (e.rank + 15) & ~15;
+      for (int idx = threadIdx.x; idx < rp * io.npa; idx += kMT) {
+        const int n = idx / io.npa;
+        const int c = idx - n * io.npa;
+        apg[idx] = pv.page_ids[e.a_off + min(n, e.rank - 1) * io.npa + c];
+      }
+    }
+    __syncthreads();
+    const bool first = i == a.tile;
+    switch ((e.rank + 15) >> 4) {
+      case 1: shrink_tile<T, 1>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+      case 2: shrink_tile<T, 2>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+      case 3: shrink_tile<T, 3>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+      case 4: shrink_tile<T, 4>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+      case 5: shrink_tile<T, 5>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+      case 6: shrink_tile<T, 6>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+      case 7: shrink_tile<T, 7>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+      default: shrink_tile<T, 8>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+    }
+  }
+}
+
+// Split API: v rows of a tile that several blocks shared: the sum of their
+// partial tiles in block order (the first one, then += the others).
+__device__ __forceinline__ void shrink_reduce_tile(const PlanView& pl, const IoDesc& io, int tile,
+                                                   int rank, float* v, int v_ld, int* toks) {
+  const int32_t* off = pl.contrib_off + io.slice * (pl.tile_cap + 1);
+  const int32_t* lst = contrib_list(pl, io.slice);
+  const int c0 = off[tile], c1 = off[tile + 1];
+  if (c1 - c0 <= 1) return;  // a single block covered the tile and wrote v
+  const PlanItem item = pl.items[tile];
+  load_tile_tokens(pl, item, toks);
+  __syncthreads();
+  const int ntb = (item.count + 15) >> 4;
+  const int nu = ((rank + 15) >> 4) * ntb * 64;
+  for (int u = threadIdx.x; u < nu; u += kMT) {
+    const int sl = unit_slot(u, ntb);
+    if (sl >= item.count) continue;
+    float4 sum = part_at(pl, 0, lst[2 * c0 + 1])[u];
+    for (int c = c0 + 1; c < c1; ++c) {
+      const float4 q = part_at(pl, 0, lst[2 * c + 1])[u];
+      sum.x += q.x;
+      sum.y += q.y;
+      sum.z += q.z;
+      sum.w += q.w;
+    }
+    v_store4(v, v_ld, toks[sl], unit_rank(u, ntb), rank, sum);
+  }
+  v_zero_tail(v, v_ld, toks, item.count, (rank + 15) & ~15);
+}
+
+// ---- expand ---------------------------------------------------------------------
+// 16-byte y pieces: PPR per 64-row chunk row, YP per thread.
+template <typename TY>
+struct YPiece {
+  static constexpr int EPP = 8;  // elements per piece
+  static __device__ __forceinline__ uint4 fma(uint4 y, const float* a, float s) {
+    const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __builtin_fmaf(s, a[2 * i], bits_to_f<TY>(w[i] & 0xffffu));
+      const float hi = __builtin_fmaf(s, a[2 * i + 1], bits_to_f<TY>(w[i] >> 16));
+      o[i] = f_to_bits<TY>(lo) | (f_to_bits<TY>(hi) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  }
+};
+template <>
+struct YPiece<float> {
+  static constexpr int EPP = 4;
+  static __device__ __forceinline__ uint4 fma(uint4 y, const float* a, float s) {
+    return make_uint4(__float_as_uint(__builtin_fmaf(s, a[0], __uint_as_float(y.x))),
+                      __float_as_uint(__builtin_fmaf(s, a[1], __uint_as_float(y.y))),
+                      __float_as_uint(__builtin_fmaf(s, a[2], __uint_as_float(y.z))),
+                      __float_as_uint(__builtin_fmaf(s, a[3], __uint_as_float(y.w))));
+  }
+};
+
+// V rows of the tile (fp32, from src rows) -> hi and lo 16-bit parts in LDS.
+template <typename T, int NK>
+__device__ __forceinline__ void load_v_tile(const float* src, int ld, bool by_token, int64_t row0,
+                                            const int* toks, int count, int rank, uint16_t* Vh,
+                                            uint16_t* Vl) {
+  constexpr int KW = 32 * NK;
+  for (int idx = threadIdx.x; idx < kTileM * KW; idx += kMT) {
+    const int slot = idx / KW;
+    const int k = idx - slot * KW;
+    float f = 0.f;
+    if (slot < count && k < rank) {
+      const int64_t row = by_token ? (int64_t)toks[slot] : row0 + slot;
+      f = src[row * ld + k];
+    }
+    uint16_t hi, lo;
+    MfmaOp<T>::split(f, hi, lo);
+    Vh[slot * kVpRow + k] = hi;
+    Vl[slot * kVpRow + k] = lo;
+  }
+}
+
+// Chunks [c0, c1) (64 output rows each) of one tile; V packed in LDS.
+template <typename T, typename TY, int NK>
+__device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry& e,
+                                              const IoDesc& io, const int* toks, int count,
+                                              int c0, int c1, const uint16_t* Vh,
+                                              const uint16_t* Vl, float* D) {
+  typedef typename MfmaOp<T>::vec vec;
+  constexpr int EPP = YPiece<TY>::EPP;
+  constexpr int PPR = 64 / EPP;              // pieces per token row of a chunk
+  constexpr int YP = kTileM * PPR / kMT;     // pieces per thread
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int ntb = (count + 15) >> 4;
+  const int d_out = io.d_out;
+  const int rs = e.rs;
+  const float s = e.scale;
+  // this thread's y pieces
+  char* yrow[YP];
+  bool yok[YP];
+  int yslot[YP], ymo[YP];
+#pragma unroll
+  for (int j = 0; j < YP; ++j) {
+    const int q = t + kMT * j;
+    yslot[j] = q / PPR;
+    ymo[j] = (q % PPR) * EPP;
+    yok[j] = yslot[j] < count;
+    yrow[j] = reinterpret_cast<char*>(io.y) +
+              (int64_t)toks[min(yslot[j], count - 1)] * d_out * (int)sizeof(TY);
+  }
+  const int q_last = (d_out - 1) / e.rpp;
+  auto loadB = [&](int c, uint4 (&bo)[NK]) {
+    // rpp >= 16 (planner): the wave's 16 rows lie on at most two pages, whose
+    // ids are scalar loads
+    const int mb0 = __builtin_amdgcn_readfirstlane(min(64 * c + 16 * w, d_out - 1));
+    const int m = min(mb0 + r16, d_out - 1);
+    const int64_t off = b_offset_wave(pv, e, 2, m, mb0, q_last);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      bo[ks] = ld16(pv.pages + off + (int64_t)min(32 * ks + 8 * g, rs - 8) * 2);
+  };
+  bool kok[NK];  // B columns past the stored row length are masked at use
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) kok[ks] = 32 * ks + 8 * g < rs;
+  auto loadY = [&](int c, uint4 (&yv)[YP]) {
+#pragma unroll
+    for (int j = 0; j < YP; ++j) {
+      const int m = min(64 * c + ymo[j], d_out - EPP);
+      yv[j] = ld16(yrow[j] + (int64_t)m * (int)sizeof(TY));
+    }
+  };
+  // Three register sets rotate by unrolling (a register copy of a load in
+  // flight would wait for it): chunk c uses set (c - c0) % 3, and the loads of
+  // chunk c + 2 are issued before chunk c is computed.  Prefetches are never
+  // skipped (see shrink_stages): past c1 they repeat the last chunk.
+  auto process = [&](int c, const uint4 (&bc)[NK], const uint4 (&yc)[YP]) {
+    f32x4_t acc[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      if (tb < ntb) {
+        const int vo = (16 * tb + r16) * kVpRow + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          const uint4 vh = *reinterpret_cast<const uint4*>(Vh + vo + 32 * ks);
+          const uint4 vl = *reinterpret_cast<const uint4*>(Vl + vo + 32 * ks);
+          const vec bk = as_vec<vec>(keep16m(bc[ks], kok[ks]));
+          acc[tb] = MfmaOp<T>::mma(bk, as_vec<vec>(vh), acc[tb]);
+          acc[tb] = MfmaOp<T>::mma(bk, as_vec<vec>(vl), acc[tb]);
+        }
+      }
+    }
+    lds_barrier();  // D is free: every wave is done with the previous chunk's RMW
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      if (tb < ntb)
+        *reinterpret_cast<float4*>(D + (16 * tb + r16) * kDsRow + 16 * w + 4 * g) =
+            make_float4(acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]);
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < YP; ++j) {
+      const int m = 64 * c + ymo[j];
+      if (yok[j] && m < d_out) {
+        float a[EPP];
+        const float* dr = D + yslot[j] * kDsRow + ymo[j];
+#pragma unroll
+        for (int i = 0; i < EPP; i += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(dr + i);
+          a[i] = q.x;
+          a[i + 1] = q.y;
+          a[i + 2] = q.z;
+          a[i + 3] = q.w;
+        }
+        *reinterpret_cast<uint4*>(yrow[j] + (int64_t)m * (int)sizeof(TY)) = YPiece<TY>::fma(yc[j], a, s);
+      }
+    }
+  };
+  uint4 b0[NK], b1[NK], b2[NK], y0[YP], y1[YP], y2[YP];
+  loadB(c0, b0);
+  loadY(c0, y0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the prologue in loop order
+  loadB(min(c0 + 1, c1 - 1), b1);
+  loadY(min(c0 + 1, c1 - 1), y1);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c = c0; c < c1; c += 3) {
+    loadB(min(c + 2, c1 - 1), b2);
+    loadY(min(c + 2, c1 - 1), y2);
+    process(c, b0, y0);
+    loadB(min(c + 3, c1 - 1), b0);
+    loadY(min(c + 3, c1 - 1), y0);
+    if (c + 1 < c1) process(c + 1, b1, y1);
+    loadB(min(c + 4, c1 - 1), b1);
+    loadY(min(c + 4, c1 - 1), y1);
+    if (c + 2 < c1) process(c + 2, b2, y2);
+  }
+}
+
+// Fused: V of a tile from its contributors' partial tiles (summed in block
+// order, as the split API's reduce does) -> hi and lo parts in LDS.  Columns
+// [16 * ceil(rank / 16), 32 * NK) and slots past the count are zero.
+template <typename T, int NK>
+__device__ __forceinline__ void load_v_parts(const PlanView& pl, int j, const int32_t* lst, int c0,
+                                             int c1, int count, int rank, uint16_t* Vh,
+                                             uint16_t* Vl) {
+  constexpr int KW = 32 * NK;
+  const int ntb = (count + 15) >> 4;
+  const int nu = ((rank + 15) >> 4) * ntb * 64;
+  for (int u = threadIdx.x; u < nu; u += kMT) {
+    const int sl = unit_slot(u, ntb);
+    const int n = unit_rank(u, ntb);
+    float4 sum = part_at(pl, j, lst[2 * c0 + 1])[u];
+    for (int c = c0 + 1; c < c1; ++c) {
+      const float4 q = part_at(pl, j, lst[2 * c + 1])[u];
+      sum.x += q.x;
+      sum.y += q.y;
+      sum.z += q.z;
+      sum.w += q.w;
+    }
+    const float a[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = (sl < count && n + i < rank) ? a[i] : 0.f;
+      uint16_t hi, lo;
+      MfmaOp<T>::split(f, hi, lo);
+      Vh[sl * kVpRow + n + i] = hi;
+      Vl[sl * kVpRow + n + i] = lo;
+    }
+  }
+  // zero: columns [16 * ceil(rank / 16), KW) of the computed slots, and all
+  // KW columns of the slots past 16 * ntb (never read: tb < ntb only)
+  const int w0 = (rank + 15) & ~15;
+  for (int idx = threadIdx.x; idx < 16 * ntb * (KW - w0); idx += kMT) {
+    const int sl = idx / (KW - w0);
+    const int k = w0 + idx - sl * (KW - w0);
+    Vh[sl * kVpRow + k] = 0;
+    Vl[sl * kVpRow + k] = 0;
+  }
+}
+
+// The block's expand range in launch slice j.  Split API: V from the caller's
+// v (rows by token).  Fused (v == null): V of a tile from its partial tiles,
+// each ready once its flag holds this launch's epoch.
+template <typename T, typename TY>
+__device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView& pl,
+                                             const IoDesc& io, int j, int L, const float* v,
+                                             int v_ld, const LdsBufs& lb) {
+  const int nch = (io.d_out + 63) / 64;
+  const Pos a = range_start(pl.bs_expand, L, nch, pl.n_mfma);
+  const Pos b = range_start(pl.bs_expand, L + 1, nch, pl.n_mfma);
+  int* toks = reinterpret_cast<int*>(lb.misc + kOffToks);
+  uint16_t* Vh = reinterpret_cast<uint16_t*>(lb.a);
+  uint16_t* Vl = reinterpret_cast<uint16_t*>(lb.b);
+  float* Ds = reinterpret_cast<float*>(lb.c);
+  for (int i = a.tile; i < pl.n_mfma && pos_lt(Pos{i, 0}, b.tile, b.k); ++i) {
+    const int c0 = i == a.tile ? a.k : 0;
+    const int c1 = i == b.tile ? b.k : nch;
+    if (c0 >= c1) continue;
+    const PlanItem item = pl.items[i];
+    const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
+    load_tile_tokens(pl, item, toks);
+    const int32_t* off = pl.contrib_off + io.slice * (pl.tile_cap + 1);
+    const int32_t* lst = contrib_list(pl, io.slice);
+    const int cb0 = off[i], cb1 = off[i + 1];
+    if (!v) {
+      for (int c = cb0 + (int)threadIdx.x; c < cb1; c += kMT) {
+        const uint32_t* f = pl.flags + j * pl.contrib_cap + c;
+        int spins = 0;
+        while (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != pl.epoch) {
+          if (++spins > (1 << 18)) {  // ~0.3 s: report and go on rather than hang
+            atomicAdd(pl.err, 1);
+            break;
           }
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    } else {
+      __syncthreads();
+    }
+    switch ((e.rs + 31) >> 5) {
+      case 1:
+        if (v) load_v_tile<T, 1>(v, v_ld, true, 0, toks, item.count, e.rank, Vh, Vl);
+        else load_v_parts<T, 1>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+        __syncthreads();
+        expand_chunks<T, TY, 1>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
+        break;
+      case 2:
+        if (v) load_v_tile<T, 2>(v, v_ld, true, 0, toks, item.count, e.rank, Vh, Vl);
+        else load_v_parts<T, 2>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+        __syncthreads();
+        expand_chunks<T, TY, 2>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
+        break;
+      case 3:
+        if (v) load_v_tile<T, 3>(v, v_ld, true, 0, toks, item.count, e.rank, Vh, Vl);
+        else load_v_parts<T, 3>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+        __syncthreads();
+        expand_chunks<T, TY, 3>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
+        break;
+      default:
+        if (v) load_v_tile<T, 4>(v, v_ld, true, 0, toks, item.count, e.rank, Vh, Vl);
+        else load_v_parts<T, 4>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+        __syncthreads();
+        expand_chunks<T, TY, 4>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
+        break;
     }
     __syncthreads();
   }
 }
-
-// ---- V (fp32 in LDS) -> packed hi/lo 16-bit operands, in place ---------------
-// Row `slot` becomes hi[0..32*NK) followed by lo[0..32*NK) (k >= rank: zero).
-template <typename T, int NK>
-__device__ __forceinline__ void pack_v_lds(float* Vs, int rank) {
-  constexpr int KW = 32 * NK;
-  constexpr int PER = kTileM * KW / 256;  // values per thread
-  const int t = threadIdx.x;
-  uint16_t hi[PER], lo[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int idx = t + 256 * j;
-    const int slot = idx / KW;
-    const int k = idx - slot * KW;
-    const float f = k < rank ? Vs[slot * kVsStride + k] : 0.f;
-    MfmaOp<T>::split(f, hi[j], lo[j]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int idx = t + 256 * j;
-    const int slot = idx / KW;
-    const int k = idx - slot * KW;
-    uint16_t* row = reinterpret_cast<uint16_t*>(Vs + slot * kVsStride);
-    row[k] = hi[j];
-    row[KW + k] = lo[j];
-  }
-  __syncthreads();
-}
-
-// 4 consecutive y elements of one row: load / store (8 bytes for 16-bit, 16 for fp32)
-template <typename TY>
-struct Y4 {
-  typedef uint2 raw;
-  static __device__ __forceinline__ uint2 load_raw(const char* row, int m) {
-    return *reinterpret_cast<const uint2*>(row + (int64_t)m * 2);
-  }
-  static __device__ __forceinline__ void unpack(const uint2 u, float (&v)[4]) {
-    v[0] = bits_to_f<TY>(u.x & 0xffffu);
-    v[1] = bits_to_f<TY>(u.x >> 16);
-    v[2] = bits_to_f<TY>(u.y & 0xffffu);
-    v[3] = bits_to_f<TY>(u.y >> 16);
-  }
-  static __device__ __forceinline__ void store(char* row, int m, const float (&v)[4]) {
-    *reinterpret_cast<uint2*>(row + (int64_t)m * 2) =
-        make_uint2(f_to_bits<TY>(v[0]) | (f_to_bits<TY>(v[1]) << 16),
-                   f_to_bits<TY>(v[2]) | (f_to_bits<TY>(v[3]) << 16));
-  }
-};
-template <>
-struct Y4<float> {
-  typedef uint4 raw;
-  static __device__ __forceinline__ uint4 load_raw(const char* row, int m) {
-    return *reinterpret_cast<const uint4*>(row + (int64_t)m * 4);
-  }
-  static __device__ __forceinline__ void unpack(const uint4 u, float (&v)[4]) {
-    v[0] = __uint_as_float(u.x);
-    v[1] = __uint_as_float(u.y);
-    v[2] = __uint_as_float(u.z);
-    v[3] = __uint_as_float(u.w);
-  }
-  static __device__ __forceinline__ void store(char* row, int m, const float (&v)[4]) {
-    *reinterpret_cast<float4*>(row + (int64_t)m * 4) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-};
-
-// ---- expand from packed V in LDS: rows [m_lo, m_hi) for all the tile's tokens --
-// m_lo is a multiple of 64 and m_hi of 8.
-template <typename T, typename TY, int NK>
-__device__ __forceinline__ void mfma_expand_lds(const PoolView& pv, const DevEntry& e,
-                                                const IoDesc& io, const int* toks, int count,
-                                                const float* Vs, int m_lo, int m_hi) {
-  typedef typename MfmaOp<T>::vec vec;
-  constexpr int ELT = 2;
-  constexpr int KW = 32 * NK;
-  constexpr int MB = 2;  // m-blocks per step per wave
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const int ntb = (count + 15) >> 4;  // token blocks with at least one token
-  const float s = e.scale;
-  const int rs = e.rs;
-  // this lane's output tokens (accumulator column = slot tb*16 + r16)
-  const int tok0 = toks[0];
-  char* yrow[4];
-  bool yok[4];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int tk = toks[tb * 16 + r16];
-    yok[tb] = tk >= 0;
-    yrow[tb] = reinterpret_cast<char*>(io.y) + (int64_t)(tk >= 0 ? tk : tok0) * io.d_out * sizeof(TY);
-  }
-  // V^T operands: column = slot, k = 32 ks + 8 g + j
-  const uint16_t* vrow[4];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-    vrow[tb] = reinterpret_cast<const uint16_t*>(Vs + (tb * 16 + r16) * kVsStride);
-  const int nmb = (m_hi - m_lo + 15) >> 4;
-  const int mlast = m_hi - 1;
-  const bool wave_pages = e.rpp >= 16;
-  const int q_last = mlast / e.rpp;
-  typedef typename Y4<TY>::raw yraw;
-  auto load_blk = [&](int b, uint4 (&bo)[NK], yraw (&yv)[4]) {
-    const int mb0 = __builtin_amdgcn_readfirstlane(m_lo + 16 * min(b, nmb - 1));
-    const int m = min(mb0 + r16, mlast);
-    const int64_t off = wave_pages ? b_offset_wave(pv, e, ELT, m, mb0, q_last) : b_offset(pv, e, ELT, m);
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      const int k = 32 * ks + 8 * g;
-      bo[ks] = keep16m(ld16(pv.pages + off + (int64_t)min(k, rs - 8) * ELT), k < rs);
-    }
-    const int mo = min(mb0 + 4 * g, m_hi - 4);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) yv[tb] = Y4<TY>::load_raw(yrow[tb], mo);
-  };
-  uint4 bc[MB][NK], bn[MB][NK];
-  yraw yc[MB][4], yn[MB][4];
-  // wave w handles m-blocks w + 4 * (MB * j + u), u < MB
-#pragma unroll
-  for (int u = 0; u < MB; ++u) load_blk(w + 4 * u, bc[u], yc[u]);
-  for (int b0 = w; b0 < nmb; b0 += 4 * MB) {
-    asm volatile("" ::: "memory");  // V operands are re-read from LDS every step
-#pragma unroll
-    for (int u = 0; u < MB; ++u) load_blk(b0 + 4 * (MB + u), bn[u], yn[u]);
-#pragma unroll
-    for (int u = 0; u < MB; ++u) {
-      const int b = b0 + 4 * u;
-      f32x4_t acc[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        asm volatile("" ::: "memory");  // one rank step of V operands live at a time
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          if (tb < ntb) {
-            const uint4 vh = *reinterpret_cast<const uint4*>(vrow[tb] + 32 * ks + 8 * g);
-            const uint4 vl = *reinterpret_cast<const uint4*>(vrow[tb] + KW + 32 * ks + 8 * g);
-            acc[tb] = MfmaOp<T>::mma(as_vec<vec>(bc[u][ks]), as_vec<vec>(vh), acc[tb]);
-            acc[tb] = MfmaOp<T>::mma(as_vec<vec>(bc[u][ks]), as_vec<vec>(vl), acc[tb]);
-          }
-        }
-      }
-      const int mo = m_lo + 16 * b + 4 * g;
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        if (tb < ntb && b < nmb && mo < m_hi && yok[tb]) {
-          float yv[4], out[4];
-          Y4<TY>::unpack(yc[u][tb], yv);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) out[i] = __builtin_fmaf(s, acc[tb][i], yv[i]);
-          Y4<TY>::store(yrow[tb], mo, out);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < MB; ++u) {
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) bc[u][ks] = bn[u][ks];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) yc[u][tb] = yn[u][tb];
-    }
-  }
-}
-
-// ---- dispatch helpers (rank-dependent template arguments) -------------------
-template <typename T, int MBT>
-__device__ __forceinline__ void mfma_shrink_any(const PoolView& pv, const DevEntry& e,
-                                                const IoDesc& io, const int* toks, int slot0,
-                                                float* Vs) {
-  switch ((e.rank + 15) >> 4) {
-    case 1: mfma_shrink_lds<T, 1, MBT>(pv, e, io, toks, slot0, Vs); break;
-    case 2: mfma_shrink_lds<T, 2, MBT>(pv, e, io, toks, slot0, Vs); break;
-    case 3: mfma_shrink_lds<T, 3, MBT>(pv, e, io, toks, slot0, Vs); break;
-    case 4: mfma_shrink_lds<T, 4, MBT>(pv, e, io, toks, slot0, Vs); break;
-    case 5: mfma_shrink_lds<T, 5, MBT>(pv, e, io, toks, slot0, Vs); break;
-    case 6: mfma_shrink_lds<T, 6, MBT>(pv, e, io, toks, slot0, Vs); break;
-    case 7: mfma_shrink_lds<T, 7, MBT>(pv, e, io, toks, slot0, Vs); break;
-    default: mfma_shrink_lds<T, 8, MBT>(pv, e, io, toks, slot0, Vs); break;
-  }
-}
-
-template <typename T, typename TY>
-__device__ __forceinline__ void mfma_pack_expand_any(const PoolView& pv, const DevEntry& e,
-                                                     const IoDesc& io, const int* toks, int count,
-                                                     float* Vs, int m_lo, int m_hi) {
-  switch ((e.rs + 31) >> 5) {
-    case 1:
-      pack_v_lds<T, 1>(Vs, e.rank);
-      mfma_expand_lds<T, TY, 1>(pv, e, io, toks, count, Vs, m_lo, m_hi);
-      break;
-    case 2:
-      pack_v_lds<T, 2>(Vs, e.rank);
-      mfma_expand_lds<T, TY, 2>(pv, e, io, toks, count, Vs, m_lo, m_hi);
-      break;
-    case 3:
-      pack_v_lds<T, 3>(Vs, e.rank);
-      mfma_expand_lds<T, TY, 3>(pv, e, io, toks, count, Vs, m_lo, m_hi);
-      break;
-    default:
-      pack_v_lds<T, 4>(Vs, e.rank);
-      mfma_expand_lds<T, TY, 4>(pv, e, io, toks, count, Vs, m_lo, m_hi);
-      break;
-  }
-}
-
-// ---- the three entry shapes ----------------------------------------------------
-// Split-API shrink of half a tile (32 slots from slot0): v rows of its tokens.
-template <typename T>
-__device__ __forceinline__ void mfma_shrink_tile(const PoolView& pv, const PlanView& pl,
-                                                 const PlanItem& item, const IoDesc& io,
-                                                 int half, float* v, int v_ld, char* lds) {
-  int* toks = reinterpret_cast<int*>(lds);
-  float* Vs = reinterpret_cast<float*>(lds + 256);
-  const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
-  load_tile_tokens(pl, item, toks);
-  __syncthreads();
-  const int slot0 = 32 * half;
-  if (slot0 >= item.count) return;
-  const int t = threadIdx.x;
-  if (e.rank <= 0) {
-    for (int idx = t; idx < 32 * v_ld; idx += 256) {
-      const int sl = slot0 + idx / v_ld;
-      if (toks[sl] >= 0) v[(int64_t)toks[sl] * v_ld + idx % v_ld] = 0.f;
-    }
-    return;
-  }
-  mfma_shrink_any<T, 2>(pv, e, io, toks, slot0, Vs);
-  const int rp = (e.rank + 15) & ~15;
-  for (int idx = t; idx < 32 * v_ld; idx += 256) {
-    const int sl = slot0 + idx / v_ld;
-    const int n = idx % v_ld;
-    const int tk = toks[sl];
-    if (tk >= 0) v[(int64_t)tk * v_ld + n] = (n < e.rank && n < rp) ? Vs[sl * kVsStride + n] : 0.f;
-  }
-}
-
-// Split-API expand of one tile over output rows [m_lo, m_hi): V from global v.
-template <typename T, typename TY>
-__device__ __forceinline__ void mfma_expand_tile(const PoolView& pv, const PlanView& pl,
-                                                 const PlanItem& item, const DevEntry& e,
-                                                 const IoDesc& io, const float* v, int v_ld,
-                                                 int m_lo, int m_hi, char* lds) {
-  int* toks = reinterpret_cast<int*>(lds);
-  float* Vs = reinterpret_cast<float*>(lds + 256);
-  load_tile_tokens(pl, item, toks);
-  __syncthreads();
-  const int KW = ((e.rs + 31) >> 5) * 32;
-  for (int idx = threadIdx.x; idx < kTileM * KW; idx += 256) {
-    const int sl = idx / KW;
-    const int k = idx - sl * KW;
-    const int tk = toks[sl];
-    Vs[sl * kVsStride + k] = (tk >= 0 && k < e.rank) ? v[(int64_t)tk * v_ld + k] : 0.f;
-  }
-  __syncthreads();
-  mfma_pack_expand_any<T, TY>(pv, e, io, toks, item.count, Vs, m_lo, m_hi);
-}
-
-// Fused tile: shrink into LDS, then expand rows [m_lo, m_hi).
-template <typename T, typename TY>
-__device__ __forceinline__ void mfma_apply_tile(const PoolView& pv, const PlanView& pl,
-                                                const PlanItem& item, const DevEntry& e,
-                                                const IoDesc& io, int m_lo, int m_hi, char* lds) {
-  int* toks = reinterpret_cast<int*>(lds);
-  float* Vs = reinterpret_cast<float*>(lds + 256);
-  load_tile_tokens(pl, item, toks);
-  __syncthreads();
-  mfma_shrink_any<T, 4>(pv, e, io, toks, 0, Vs);
-  mfma_pack_expand_any<T, TY>(pv, e, io, toks, item.count, Vs, m_lo, m_hi);
-}
-
-constexpr int kMfmaLds = 256 + kVsBytes;
 
 }  // namespace lora

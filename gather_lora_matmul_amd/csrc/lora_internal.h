@@ -66,6 +66,8 @@ struct PlanItem {
 
 constexpr int kShortG = 4;   // tokens per short item
 constexpr int kTileM = 64;   // tokens per MFMA tile
+constexpr int kVgLd = LORA_MAX_RANK;  // floats per slot of a partial tile
+constexpr int kMaxNpa = 8;            // MFMA tiles: pages per A row, at most
 
 // ---- kernel launchers (defined in the .hip files) -------------------------
 hipError_t launch_fill_pages(char* pages, int64_t page_bytes, const int32_t* ids_dev,
@@ -84,14 +86,41 @@ hipError_t launch_bgmv_expand(int dtype, int y_dtype, const PoolView& pv, const 
 hipError_t launch_bgmv_apply(int dtype, int y_dtype, const PoolView& pv, const IoSet& ios,
                              const int32_t* ids, int32_t n, hipStream_t s);
 
+// Start of one block's share of the MFMA tiles (persistent kernels): the tile
+// holding the block's first unit of work and the offset into that tile in
+// weight units (w = the tile's weight per stage or chunk).  In a slice whose
+// tiles have n stages (or chunks), the block starts at stage ceil(n*off/w) of
+// `tile`; consecutive entries delimit a block's range.
+struct BlockStart {
+  int32_t tile;
+  int32_t off;
+  int32_t w;
+  int32_t pad;
+};
+
 // Items [0, n_mfma) are MFMA tiles, [n_mfma, n_items) short items.
 struct PlanView {
   const PlanItem* items;
   const int32_t* perm;
+  const BlockStart* bs_shrink;   // [G + 1]
+  const BlockStart* bs_expand;   // [G + 1]
+  // split-K contributors of each MFMA tile's shrink, per pool slice s: the
+  // entries [contrib_off[s][i], contrib_off[s][i + 1]) of contrib[s] list the
+  // blocks whose shrink ranges meet tile i, in block order, as pairs
+  // {(L << 1) | side, float4 offset of the contribution's partial tile}
+  const int32_t* contrib_off;    // [n_slices][tile_cap + 1]
+  const int32_t* contrib;        // [n_slices][contrib_cap][2]
+  float* part;                   // partial tiles [n_io][part_stride] float4
+  uint32_t* flags;               // fused: per (launch slice, contributor) ready epochs [LORA_MAX_IO][contrib_cap]
+  int32_t* err;                  // [1]: bounded waits that timed out
   int32_t n_items;
   int32_t n_tokens;
   int32_t n_mfma;
-  int32_t pad;
+  int32_t G;                     // persistent grid (blocks)
+  int32_t tile_cap;              // max tiles = max tokens
+  int32_t contrib_cap;           // entries of contrib per slice
+  int64_t part_stride;           // float4 units of partial tiles per launch slice
+  uint32_t epoch;                // fused launch number (flags compare against it)
 };
 
 hipError_t launch_sgmv_shrink(int dtype, const PoolView& pv, const PlanView& pl,

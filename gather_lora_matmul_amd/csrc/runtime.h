@@ -95,6 +95,13 @@ struct lora_pool {
   }
 };
 
+struct lora_plan;
+namespace lora {
+// Grow the plan's split-K partial workspace to hold n_io slices (allocation
+// happens at most once per size increase; the first launches pay for it).
+lora_status plan_reserve_part(lora_plan* pl, int n_io);
+}  // namespace lora
+
 struct lora_plan {
   lora_pool* pool = nullptr;
   int32_t max_tokens = 0;
@@ -114,14 +121,38 @@ struct lora_plan {
   bool ev_pending = false;
   int32_t* d_perm = nullptr;
   lora::PlanItem* d_items = nullptr;
+  // persistent MFMA kernels: grid, block-range tables and device work buffers
+  int32_t G = 0;
+  std::vector<lora::BlockStart> h_bs;       // [2][G + 1]: shrink, expand
+  lora::BlockStart* d_bs = nullptr;
+  int32_t contrib_cap = 0;                  // per slice: 2 G + max_tokens + 8
+  int64_t part_stride = 0;                  // float4 units of partial tiles per launch slice
+  std::vector<int32_t> h_contrib;           // [n_slices][max_tokens + 1] offsets, then [n_slices][contrib_cap][2]
+  int32_t* d_contrib = nullptr;
+  uint32_t* d_flags = nullptr;              // [LORA_MAX_IO][contrib_cap]
+  int32_t* d_err = nullptr;                 // [1]
+  float* d_part = nullptr;                  // grown on demand: [n_io][part_stride] float4
+  size_t part_cap = 0;                      // floats
+  uint32_t epoch = 0;                       // last fused launch number
   lora::PlanView view() const {
     lora::PlanView v;
     v.items = d_items;
     v.perm = d_perm;
+    v.bs_shrink = d_bs;
+    v.bs_expand = d_bs ? d_bs + (G + 1) : nullptr;
+    v.contrib_off = d_contrib;
+    v.contrib = d_contrib ? d_contrib + (size_t)pool->n_slices * (max_tokens + 1) : nullptr;
+    v.contrib_cap = contrib_cap;
+    v.part_stride = part_stride;
+    v.part = d_part;
+    v.flags = d_flags;
+    v.err = d_err;
     v.n_items = n_items;
     v.n_tokens = n_tokens;
     v.n_mfma = n_mfma;
-    v.pad = 0;
+    v.G = G;
+    v.tile_cap = max_tokens;
+    v.epoch = epoch;
     return v;
   }
 };

@@ -182,7 +182,11 @@ typedef struct {
   int32_t l_long;       /* group length from which MFMA tiles are used           */
 } lora_plan_stats;
 
-/* Plan for up to max_tokens tokens (device buffers allocated once). */
+/* Plan for up to max_tokens tokens (device buffers allocated once; on 16-bit
+ * pools about 4.1 KB per token for the fused V rows and tile counters, plus a
+ * split-K workspace of 64 KB per block and slice grown at first use).  A plan
+ * is used by one stream at a time: launches that use the same plan must not
+ * overlap (they share its counters and workspaces). */
 lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** out);
 lora_status lora_plan_destroy(lora_plan* plan);
 /* Build the plan of one batch from host ids [n] (any order, -1 = no adapter):
@@ -201,6 +205,11 @@ lora_status lora_plan_get_stats(const lora_plan* plan, lora_plan_stats* out);
  * and items [n_items][4] = {adapter, start in perm, count, kind (0 short,
  * 1 MFMA tile)}.  Either pointer may be NULL. */
 lora_status lora_plan_export(const lora_plan* plan, int32_t* perm_host, int32_t* items_host);
+/* Number of bounded in-kernel waits (lora_apply on MFMA tiles waits for the V
+ * tiles other blocks produce) that gave up instead of finishing; nonzero means
+ * the outputs of those launches are invalid.  Blocks until all device work is
+ * done (it synchronizes the device). */
+lora_status lora_plan_check(const lora_plan* plan, int32_t* n_timeouts);
 
 /* Shrink for a planned batch: v[i][.] as lora_bgmv_shrink (rows indexed by the
  * original token index). */

@@ -188,7 +188,11 @@ def test_planner_groups_the_index_vector_example():
 @pytest.mark.parametrize("l_long", [0, 1, 1 << 30])
 def test_planner_invariants(l_long):
     rng = np.random.default_rng(7)
-    wl = W.small_workload("bf16", 64, 64, list(rng.choice([8, 16, 64, 40], 50)), 64)
+    # P = 1024: ranks up to 64 leave >= 16 B rows per page (MFMA tiles);
+    # rank 96 does not, and its groups stay short items whatever their length
+    ranks = list(rng.choice([8, 16, 64, 40, 96], 50))
+    ranks[3], ranks[9] = 64, 96
+    wl = W.small_workload("bf16", 64, 64, ranks, 1024)
     ids = np.concatenate([np.full(150, 3), rng.integers(-1, 50, 400), np.full(70, 9)]).astype(np.int32)
     rng.shuffle(ids)
     sp, plan = _plan_for(wl, ids, l_long)
@@ -197,15 +201,23 @@ def test_planner_invariants(l_long):
     covered = np.zeros(len(ids), int)
     eff = 1 if l_long <= 0 else l_long
     counts = {a: int(np.sum(ids == a)) for a in set(ids.tolist())}
+
+    def tile_layout_ok(a):  # stored B row = rank rounded up to 8 elements
+        return 1024 // ((int(ranks[a]) + 7) // 8 * 8) >= 16
+
+    n_tiles = 0
     for a, start, count, kind in items.tolist():
         toks = perm[start:start + count]
         covered[toks] += 1
         assert np.all(ids[toks] == a) or (a == -1 and np.all(ids[toks] < 0))
         assert np.all(np.diff(toks) > 0)           # stable: original order inside a group
         if kind == 1:
-            assert a >= 0 and count <= 64 and counts[a] >= eff
+            assert a >= 0 and count <= 64 and counts[a] >= eff and tile_layout_ok(a)
+            n_tiles += 1
         else:
-            assert count <= 4 and (a < 0 or counts[a] < eff)
+            assert count <= 4 and (a < 0 or counts[a] < eff or not tile_layout_ok(a))
+    if l_long < (1 << 30):
+        assert n_tiles > 0 and not any(it[0] == 9 and it[3] == 1 for it in items.tolist())
     assert np.all(covered == 1)
     kinds = items[:, 3]
     assert np.all(np.diff(kinds) <= 0)              # MFMA tiles first

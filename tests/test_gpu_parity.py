@@ -79,6 +79,7 @@ def run_sgmv(sp, batch, slices, y_dtype, mode, l_long=0):
         L.lora_apply(sp.handle, plan, [(s, xs[s], ys[s].view) for s in slices], ydt)
     torch.cuda.synchronize()
     stats = L.lora_plan_get_stats(plan)
+    assert L.lora_plan_check(plan) == 0, "fused launch gave up waiting for a V tile"
     L.lora_plan_destroy(plan)
     return {s: ys[s].host() for s in slices}, stats
 
@@ -238,6 +239,9 @@ SMALL_SGMV = [
     ("bf16", 256, 520, [16, 64, 5, 128], 256, [0] * 70 + [1] * 17 + [2] * 3 + [3] * 130 + [-1] * 5),
     ("f16", 512, 264, [8, 40, 1], 256, [1] * 33 + [0, 2, 1, 0] * 9 + [2] * 16),
     ("f32", 256, 256, [4, 8, 8, 16], 256, [0, 1, 2, 3] * 10 + [3] * 20),
+    # pages large enough for every rank on MFMA tiles; A rows over two pages
+    ("bf16", 2304, 1000, [128, 16, 64, 5, 96], 2048,
+     [0] * 150 + [1] * 65 + [2] * 7 + [3] * 1 + [4] * 40 + [-1] * 3),
 ]
 
 
@@ -273,6 +277,43 @@ def test_sgmv_exact_small_bit_exact(mode):
     exact_compare(ys[0], reference(wl, b, 0, "bf16"), "bf16", "sgmv exact small")
     y_b = run_bgmv(sp, b, [0], "bf16", "fused")[0]
     assert y_b.tobytes() == ys[0].tobytes()
+
+
+def test_sgmv_plan_reuse_repeated_launches():
+    # one plan, several launches in a row: fused (launch epochs), split (stage
+    # counters reset by the reducing block), fused again -- all bit-identical
+    dtype, d_in, d_out, ranks, P, ids = SMALL_SGMV[0]
+    log("[case] sgmv plan reuse")
+    wl = W.small_workload(dtype, d_in, d_out, ranks, P, n_slices=2, seed=40)
+    ids = np.array(ids, np.int32)
+    np.random.default_rng(3).shuffle(ids)
+    b = W.custom_batch(wl, ids)
+    sp = pool_for(("small", 0), wl)
+    n = len(ids)
+    plan = L.lora_plan_create(sp.handle, n)
+    try:
+        L.lora_plan_build(plan, b.ids)
+        xs = [to_device(b.x[s], dtype) for s in range(2)]
+        ydt = W.DTYPE_CODE[dtype]
+        outs = []
+        for rep in range(5):
+            ys = [Guarded(b.y0[s], dtype) for s in range(2)]
+            if rep in (2, 3):
+                v = torch.zeros((n, sp.max_rank), device="cuda")
+                for s in range(2):
+                    L.lora_sgmv_shrink(sp.handle, plan, s, xs[s], v)
+                    L.lora_sgmv_expand(sp.handle, plan, s, v, ys[s].view, ydt)
+            else:
+                L.lora_apply(sp.handle, plan, [(s, xs[s], ys[s].view) for s in range(2)], ydt)
+            torch.cuda.synchronize()
+            outs.append([ys[s].host() for s in range(2)])
+        assert L.lora_plan_check(plan) == 0
+    finally:
+        L.lora_plan_destroy(plan)
+    for s in range(2):
+        compare(outs[0][s], reference(wl, b, s, dtype), dtype, "plan reuse s%d" % s)
+        for rep in range(1, 5):
+            assert outs[rep][s].tobytes() == outs[0][s].tobytes(), "launch %d differs" % rep
 
 
 def test_sgmv_llama13b_prefill_full():
