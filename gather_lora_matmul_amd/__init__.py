@@ -34,7 +34,7 @@ EXPORTS = (
     "lora_pool_free_pages", "lora_pool_upload", "lora_pool_evict", "lora_page_table_build",
     "lora_pool_export_entry", "lora_pool_read_pages", "lora_bgmv_shrink", "lora_bgmv_expand",
     "lora_bgmv_apply", "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
-    "lora_plan_get_stats", "lora_plan_export", "lora_plan_check", "lora_sgmv_shrink", "lora_sgmv_expand",
+    "lora_plan_get_stats", "lora_plan_export", "lora_sgmv_shrink", "lora_sgmv_expand",
     "lora_apply", "lora_debug_resolve", "lora_debug_gather", "lora_last_error",
 )
 
@@ -90,7 +90,6 @@ def _load() -> ctypes.CDLL:
         "lora_plan_build": [V, V, I32, I32, V],
         "lora_plan_get_stats": [V, ctypes.POINTER(PlanStats)],
         "lora_plan_export": [V, V, V],
-        "lora_plan_check": [V, ctypes.POINTER(I32)],
         "lora_sgmv_shrink": [V, V, I32, V, V, I32, V],
         "lora_sgmv_expand": [V, V, I32, V, I32, V, I32, V],
         "lora_apply": [V, V, I32, ctypes.POINTER(Io), I32, V],
@@ -288,13 +287,6 @@ def lora_plan_get_stats(plan: int) -> dict:
     s = PlanStats()
     _check(_lib.lora_plan_get_stats(plan, ctypes.byref(s)), "lora_plan_get_stats")
     return {f: getattr(s, f) for f, _ in PlanStats._fields_}
-
-
-def lora_plan_check(plan: int) -> int:
-    """Bounded in-kernel waits that gave up (synchronizes the device)."""
-    n = ctypes.c_int32(0)
-    _check(_lib.lora_plan_check(plan, ctypes.byref(n)), "lora_plan_check")
-    return int(n.value)
 
 
 def lora_plan_export(plan: int) -> Tuple[np.ndarray, np.ndarray]:

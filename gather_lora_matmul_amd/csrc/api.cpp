@@ -156,11 +156,7 @@ lora_status lora_apply(lora_pool* p, const lora_plan* pl, int32_t n_io, const lo
   IoSet ios;
   LORA_TRY(build_ioset(p, n_io, io, ios));
   if (pl->n_tokens == 0) return LORA_OK;
-  lora_plan* mp = const_cast<lora_plan*>(pl);  // launch state: epoch and workspace
-  if (pl->n_mfma > 0) {
-    LORA_TRY(plan_reserve_part(mp, n_io));
-    if (++mp->epoch == 0) mp->epoch = 1;  // flags start at 0
-  }
+  if (pl->n_mfma > 0) LORA_TRY(plan_reserve_part(const_cast<lora_plan*>(pl), n_io));
   return hip_status(launch_apply(p->dtype, y_dtype, p->view(), pl->view(), ios, (hipStream_t)stream),
                     "apply");
 }

@@ -172,12 +172,12 @@ __global__ __launch_bounds__(kMT, 2) void k_sgmv_expand_tiles(PoolView pv, PlanV
   expand_range<T, TY>(pv, pl, io, 0, L, v, v_ld, LdsBufs{misc, ba, bb, bc});
 }
 
-// Fused: every block first runs its shrink range of every slice (partial tiles,
-// each flagged with the launch epoch), then its expand range, waiting per tile
-// for its contributors' flags.  Launched cooperatively, so all G blocks are
-// resident and every wait ends.
-template <typename T, typename TY>
-__global__ __launch_bounds__(kMT, 2) void k_apply_tiles(PoolView pv, PlanView pl, IoSet ios) {
+// Fused apply on MFMA tiles: two launches on one stream.  The first runs every
+// block's shrink range of every slice and keeps each contribution as a partial
+// tile; the second runs the expand ranges, V of a tile being the sum of its
+// partial tiles (block order).  v itself is never materialized.
+template <typename T>
+__global__ __launch_bounds__(kMT, 2) void k_apply_shrink_tiles(PoolView pv, PlanView pl, IoSet ios) {
   __shared__ __attribute__((aligned(16))) char misc[kMiscB];
   __shared__ __attribute__((aligned(16))) char ba[kBufB];
   __shared__ __attribute__((aligned(16))) char bb[kBufB];
@@ -185,6 +185,16 @@ __global__ __launch_bounds__(kMT, 2) void k_apply_tiles(PoolView pv, PlanView pl
   const int L = logical_block(blockIdx.x, pl.G);
   const LdsBufs lb{misc, ba, bb, bc};
   for (int j = 0; j < ios.n_io; ++j) shrink_range<T>(pv, pl, ios.io[j], j, L, nullptr, 0, lb);
+}
+
+template <typename T, typename TY>
+__global__ __launch_bounds__(kMT, 2) void k_apply_expand_tiles(PoolView pv, PlanView pl, IoSet ios) {
+  __shared__ __attribute__((aligned(16))) char misc[kOffApg];
+  __shared__ __attribute__((aligned(16))) char ba[kVpB];
+  __shared__ __attribute__((aligned(16))) char bb[kVpB];
+  __shared__ __attribute__((aligned(16))) char bc[kDsB];
+  const int L = logical_block(blockIdx.x, pl.G);
+  const LdsBufs lb{misc, ba, bb, bc};
   for (int j = 0; j < ios.n_io; ++j) expand_range<T, TY>(pv, pl, ios.io[j], j, L, nullptr, 0, lb);
 }
 
@@ -199,16 +209,6 @@ inline int pick_nsplit(int units, int d_out, int target, int min_rows) {
   int nsplit = 1;
   while ((long)units * nsplit < target && d_out / (nsplit * 2) >= min_rows) nsplit *= 2;
   return nsplit;
-}
-
-// The fused tile kernel needs all G blocks resident at once.
-hipError_t cooperative_ok(const void* kernel, int G) {
-  int dev = 0, ncu = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kMT, 0);
-  if (e != hipSuccess) return e;
-  return (long)per_cu * ncu >= G ? hipSuccess : hipErrorCooperativeLaunchTooLarge;
 }
 
 template <typename T>
@@ -260,14 +260,8 @@ hipError_t apply_t(const PoolView& pv, const PlanView& pl, const IoSet& ios, hip
   const int n_short = pl.n_items - pl.n_mfma;
   if constexpr (ET<T>::bytes == 2) {
     if (pl.n_mfma > 0) {
-      hipError_t e = cooperative_ok((const void*)k_apply_tiles<T, TY>, pl.G);
-      if (e != hipSuccess) return e;
-      PoolView a0 = pv;
-      PlanView a1 = pl;
-      IoSet a2 = ios;
-      void* args[] = {&a0, &a1, &a2};
-      e = hipLaunchCooperativeKernel((const void*)k_apply_tiles<T, TY>, dim3(pl.G), dim3(kMT), args, 0, s);
-      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((k_apply_shrink_tiles<T>), dim3(pl.G), dim3(kMT), 0, s, pv, pl, ios);
+      hipLaunchKernelGGL((k_apply_expand_tiles<T, TY>), dim3(pl.G), dim3(kMT), 0, s, pv, pl, ios);
     }
   }
   if (n_short > 0) {

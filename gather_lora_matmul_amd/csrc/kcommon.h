@@ -98,12 +98,12 @@ __device__ __forceinline__ float dot16v(const uint4 a, const float* v, float acc
 }
 
 // ---- scalar y access -------------------------------------------------------
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 template <typename TY>
 __device__ __forceinline__ float load_y(const void* base, int64_t idx);
@@ -156,6 +156,20 @@ __device__ __forceinline__ uint32_t f_to_bits<bf16_t>(float f) {
 template <>
 __device__ __forceinline__ uint32_t f_to_bits<f16_t>(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// Two fp32 -> two 16-bit values (RNE) packed lo | hi << 16: one conversion
+// instruction for bf16.
+template <typename TY>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <>
+__device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---- page-table resolution ---------------------------------------------------

@@ -298,7 +298,7 @@ __device__ __forceinline__ void v_zero_tail(float* v, int v_ld, const int* toks,
 // One tile of the block's shrink range: stages [k0, k1) of nst.  Split API
 // (v != null): a block that covers the whole tile writes v; others write their
 // partial tile, summed by the reduce kernel.  Fused (v == null): every
-// contribution is a partial tile, flagged with the launch epoch once written.
+// contribution is a partial tile, summed when the expand loads V.
 template <typename T, int NB>
 __device__ __forceinline__ void shrink_tile(const PoolView& pv, const PlanView& pl,
                                             const DevEntry& e, const IoDesc& io, int j, int L,
@@ -337,12 +337,6 @@ __device__ __forceinline__ void shrink_tile(const PoolView& pv, const PlanView& 
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         part[(nb * ntb + w) * 64 + lane] = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
-    }
-    if (!v) {
-      __syncthreads();  // the block's partial stores are done
-      if (t == 0)
-        __hip_atomic_store(pl.flags + j * pl.contrib_cap + c, pl.epoch, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   __syncthreads();
@@ -429,7 +423,7 @@ struct YPiece {
     for (int i = 0; i < 4; ++i) {
       const float lo = __builtin_fmaf(s, a[2 * i], bits_to_f<TY>(w[i] & 0xffffu));
       const float hi = __builtin_fmaf(s, a[2 * i + 1], bits_to_f<TY>(w[i] >> 16));
-      o[i] = f_to_bits<TY>(lo) | (f_to_bits<TY>(hi) << 16);
+      o[i] = pack2<TY>(lo, hi);
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
   }
@@ -445,24 +439,32 @@ struct YPiece<float> {
   }
 };
 
-// V rows of the tile (fp32, from src rows) -> hi and lo 16-bit parts in LDS.
+// Split API: V rows of the tile (fp32, the caller's v by token) -> hi and lo
+// 16-bit parts in LDS.  All of a thread's loads are issued before any is used.
 template <typename T, int NK>
-__device__ __forceinline__ void load_v_tile(const float* src, int ld, bool by_token, int64_t row0,
-                                            const int* toks, int count, int rank, uint16_t* Vh,
-                                            uint16_t* Vl) {
+__device__ __forceinline__ void load_v_tile(const float* v, int v_ld, const int* toks, int count,
+                                            int rank, uint16_t* Vh, uint16_t* Vl) {
   constexpr int KW = 32 * NK;
-  for (int idx = threadIdx.x; idx < kTileM * KW; idx += kMT) {
-    const int slot = idx / KW;
-    const int k = idx - slot * KW;
-    float f = 0.f;
-    if (slot < count && k < rank) {
-      const int64_t row = by_token ? (int64_t)toks[slot] : row0 + slot;
-      f = src[row * ld + k];
+  constexpr int PER = kTileM * KW / kMT;  // 8, 16, 24 or 32
+  for (int q0 = 0; q0 < PER; q0 += 8) {
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = threadIdx.x + kMT * (q0 + q);
+      const int slot = idx / KW;
+      const int k = idx - slot * KW;
+      f[q] = v[(int64_t)toks[min(slot, count - 1)] * v_ld + min(k, rank - 1)];
     }
-    uint16_t hi, lo;
-    MfmaOp<T>::split(f, hi, lo);
-    Vh[slot * kVpRow + k] = hi;
-    Vl[slot * kVpRow + k] = lo;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = threadIdx.x + kMT * (q0 + q);
+      const int slot = idx / KW;
+      const int k = idx - slot * KW;
+      uint16_t hi, lo;
+      MfmaOp<T>::split((slot < count && k < rank) ? f[q] : 0.f, hi, lo);
+      Vh[slot * kVpRow + k] = hi;
+      Vl[slot * kVpRow + k] = lo;
+    }
   }
 }
 
@@ -588,37 +590,52 @@ __device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry
 
 // Fused: V of a tile from its contributors' partial tiles (summed in block
 // order, as the split API's reduce does) -> hi and lo parts in LDS.  Columns
-// [16 * ceil(rank / 16), 32 * NK) and slots past the count are zero.
+// [16 * ceil(rank / 16), 32 * NK) and slots past the count are zero.  Each
+// thread owns at most 8 units; a contributor's units are loaded together.
 template <typename T, int NK>
 __device__ __forceinline__ void load_v_parts(const PlanView& pl, int j, const int32_t* lst, int c0,
                                              int c1, int count, int rank, uint16_t* Vh,
                                              uint16_t* Vl) {
   constexpr int KW = 32 * NK;
   const int ntb = (count + 15) >> 4;
-  const int nu = ((rank + 15) >> 4) * ntb * 64;
-  for (int u = threadIdx.x; u < nu; u += kMT) {
-    const int sl = unit_slot(u, ntb);
-    const int n = unit_rank(u, ntb);
-    float4 sum = part_at(pl, j, lst[2 * c0 + 1])[u];
-    for (int c = c0 + 1; c < c1; ++c) {
-      const float4 q = part_at(pl, j, lst[2 * c + 1])[u];
-      sum.x += q.x;
-      sum.y += q.y;
-      sum.z += q.z;
-      sum.w += q.w;
-    }
-    const float a[4] = {sum.x, sum.y, sum.z, sum.w};
+  const int nu = ((rank + 15) >> 4) * ntb * 64;  // <= 8 * 4 * 64
+  float4 sum[8];
+  for (int c = c0; c < c1; ++c) {
+    const float4* src = part_at(pl, j, lst[2 * c + 1]);
+    float4 q[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float f = (sl < count && n + i < rank) ? a[i] : 0.f;
-      uint16_t hi, lo;
-      MfmaOp<T>::split(f, hi, lo);
-      Vh[sl * kVpRow + n + i] = hi;
-      Vl[sl * kVpRow + n + i] = lo;
+    for (int i = 0; i < 8; ++i) q[i] = src[min((int)threadIdx.x + kMT * i, nu - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (c == c0) {
+        sum[i] = q[i];
+      } else {
+        sum[i].x += q[i].x;
+        sum[i].y += q[i].y;
+        sum[i].z += q[i].z;
+        sum[i].w += q[i].w;
+      }
     }
   }
-  // zero: columns [16 * ceil(rank / 16), KW) of the computed slots, and all
-  // KW columns of the slots past 16 * ntb (never read: tb < ntb only)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int u = threadIdx.x + kMT * i;
+    if (u < nu) {
+      const int sl = unit_slot(u, ntb);
+      const int n = unit_rank(u, ntb);
+      const float a[4] = {sum[i].x, sum[i].y, sum[i].z, sum[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = (sl < count && n + e < rank) ? a[e] : 0.f;
+        uint16_t hi, lo;
+        MfmaOp<T>::split(f, hi, lo);
+        Vh[sl * kVpRow + n + e] = hi;
+        Vl[sl * kVpRow + n + e] = lo;
+      }
+    }
+  }
+  // zero: columns [16 * ceil(rank / 16), KW) of the computed slots (slots past
+  // 16 * ntb are never read: tb < ntb only)
   const int w0 = (rank + 15) & ~15;
   for (int idx = threadIdx.x; idx < 16 * ntb * (KW - w0); idx += kMT) {
     const int sl = idx / (KW - w0);
@@ -630,7 +647,7 @@ __device__ __forceinline__ void load_v_parts(const PlanView& pl, int j, const in
 
 // The block's expand range in launch slice j.  Split API: V from the caller's
 // v (rows by token).  Fused (v == null): V of a tile from its partial tiles,
-// each ready once its flag holds this launch's epoch.
+// written by the shrink launch that precedes this one on the stream.
 template <typename T, typename TY>
 __device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView& pl,
                                              const IoDesc& io, int j, int L, const float* v,
@@ -652,44 +669,28 @@ __device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView&
     const int32_t* off = pl.contrib_off + io.slice * (pl.tile_cap + 1);
     const int32_t* lst = contrib_list(pl, io.slice);
     const int cb0 = off[i], cb1 = off[i + 1];
-    if (!v) {
-      for (int c = cb0 + (int)threadIdx.x; c < cb1; c += kMT) {
-        const uint32_t* f = pl.flags + j * pl.contrib_cap + c;
-        int spins = 0;
-        while (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != pl.epoch) {
-          if (++spins > (1 << 18)) {  // ~0.3 s: report and go on rather than hang
-            atomicAdd(pl.err, 1);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(4);
-        }
-      }
-      __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    } else {
-      __syncthreads();
-    }
+    __syncthreads();
     switch ((e.rs + 31) >> 5) {
       case 1:
-        if (v) load_v_tile<T, 1>(v, v_ld, true, 0, toks, item.count, e.rank, Vh, Vl);
+        if (v) load_v_tile<T, 1>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
         else load_v_parts<T, 1>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
         __syncthreads();
         expand_chunks<T, TY, 1>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
         break;
       case 2:
-        if (v) load_v_tile<T, 2>(v, v_ld, true, 0, toks, item.count, e.rank, Vh, Vl);
+        if (v) load_v_tile<T, 2>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
         else load_v_parts<T, 2>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
         __syncthreads();
         expand_chunks<T, TY, 2>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
         break;
       case 3:
-        if (v) load_v_tile<T, 3>(v, v_ld, true, 0, toks, item.count, e.rank, Vh, Vl);
+        if (v) load_v_tile<T, 3>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
         else load_v_parts<T, 3>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
         __syncthreads();
         expand_chunks<T, TY, 3>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
         break;
       default:
-        if (v) load_v_tile<T, 4>(v, v_ld, true, 0, toks, item.count, e.rank, Vh, Vl);
+        if (v) load_v_tile<T, 4>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
         else load_v_parts<T, 4>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
         __syncthreads();
         expand_chunks<T, TY, 4>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);

@@ -111,8 +111,6 @@ struct PlanView {
   const int32_t* contrib_off;    // [n_slices][tile_cap + 1]
   const int32_t* contrib;        // [n_slices][contrib_cap][2]
   float* part;                   // partial tiles [n_io][part_stride] float4
-  uint32_t* flags;               // fused: per (launch slice, contributor) ready epochs [LORA_MAX_IO][contrib_cap]
-  int32_t* err;                  // [1]: bounded waits that timed out
   int32_t n_items;
   int32_t n_tokens;
   int32_t n_mfma;
@@ -120,7 +118,6 @@ struct PlanView {
   int32_t tile_cap;              // max tiles = max tokens
   int32_t contrib_cap;           // entries of contrib per slice
   int64_t part_stride;           // float4 units of partial tiles per launch slice
-  uint32_t epoch;                // fused launch number (flags compare against it)
 };
 
 hipError_t launch_sgmv_shrink(int dtype, const PoolView& pv, const PlanView& pl,

@@ -148,12 +148,6 @@ lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** ou
     if (e == hipSuccess) e = hipMalloc((void**)&pl->d_bs, sizeof(BlockStart) * 2 * ((size_t)pl->G + 1));
     if (pool->dtype != LORA_F32) {  // MFMA tiles exist only on 16-bit pools
       if (e == hipSuccess) e = hipMalloc((void**)&pl->d_contrib, sizeof(int32_t) * ncontrib);
-      const size_t nflags = (size_t)LORA_MAX_IO * pl->contrib_cap;
-      if (e == hipSuccess) e = hipMalloc((void**)&pl->d_flags, sizeof(uint32_t) * nflags);
-      if (e == hipSuccess) e = hipMalloc((void**)&pl->d_err, sizeof(int32_t));
-      if (e == hipSuccess) e = hipMemset(pl->d_flags, 0, sizeof(uint32_t) * nflags);
-      if (e == hipSuccess) e = hipMemset(pl->d_err, 0, sizeof(int32_t));
-      if (e == hipSuccess) e = hipDeviceSynchronize();
     }
     if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->ev, hipEventDisableTiming);
     if (e != hipSuccess) {
@@ -178,8 +172,6 @@ lora_status lora_plan_destroy(lora_plan* pl) {
   if (pl->d_perm) (void)hipFree(pl->d_perm);
   if (pl->d_items) (void)hipFree(pl->d_items);
   if (pl->d_bs) (void)hipFree(pl->d_bs);
-  if (pl->d_flags) (void)hipFree(pl->d_flags);
-  if (pl->d_err) (void)hipFree(pl->d_err);
   if (pl->d_part) (void)hipFree(pl->d_part);
   if (pl->d_contrib) (void)hipFree(pl->d_contrib);
   delete pl;
@@ -277,7 +269,8 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
       // a stage costs about one memory round trip whatever it moves: a large
       // fixed part plus half the rows
       ws[(size_t)i] = 64 + (16 * ((it.count + 15) / 16) + rp) / 2;
-      we[(size_t)i] = 2 * it.count + p->rs_of(rmax) + 16;
+      // an expand chunk: likewise a large fixed part, plus y and B rows
+      we[(size_t)i] = 256 + 2 * it.count + p->rs_of(rmax) / 2;
       tu[(size_t)i] = (rp / 16) * ((it.count + 15) / 16) * 64;
     }
     pl->h_bs.assign(2 * ((size_t)pl->G + 1), BlockStart{0, 0, 1, 0});
@@ -328,18 +321,6 @@ lora_status lora_plan_get_stats(const lora_plan* pl, lora_plan_stats* out) {
   out->n_mfma_items = pl->n_mfma;
   out->mfma_tokens = pl->mfma_tokens;
   out->l_long = pl->l_long;
-  return LORA_OK;
-}
-
-// Bounded waits of the fused kernel that gave up (0 unless a launch could not
-// make progress); waits for the plan's work on every stream.
-lora_status lora_plan_check(const lora_plan* pl, int32_t* n_timeouts) {
-  clear_error();
-  if (!pl || !n_timeouts) return fail(LORA_E_ARG, "null argument");
-  *n_timeouts = 0;
-  if (!pl->d_err) return LORA_OK;
-  LORA_HIP(hipDeviceSynchronize());
-  LORA_HIP(hipMemcpy(n_timeouts, pl->d_err, sizeof(int32_t), hipMemcpyDeviceToHost));
   return LORA_OK;
 }
 

@@ -129,11 +129,8 @@ struct lora_plan {
   int64_t part_stride = 0;                  // float4 units of partial tiles per launch slice
   std::vector<int32_t> h_contrib;           // [n_slices][max_tokens + 1] offsets, then [n_slices][contrib_cap][2]
   int32_t* d_contrib = nullptr;
-  uint32_t* d_flags = nullptr;              // [LORA_MAX_IO][contrib_cap]
-  int32_t* d_err = nullptr;                 // [1]
   float* d_part = nullptr;                  // grown on demand: [n_io][part_stride] float4
   size_t part_cap = 0;                      // floats
-  uint32_t epoch = 0;                       // last fused launch number
   lora::PlanView view() const {
     lora::PlanView v;
     v.items = d_items;
@@ -145,14 +142,11 @@ struct lora_plan {
     v.contrib_cap = contrib_cap;
     v.part_stride = part_stride;
     v.part = d_part;
-    v.flags = d_flags;
-    v.err = d_err;
     v.n_items = n_items;
     v.n_tokens = n_tokens;
     v.n_mfma = n_mfma;
     v.G = G;
     v.tile_cap = max_tokens;
-    v.epoch = epoch;
     return v;
   }
 };

@@ -183,10 +183,11 @@ typedef struct {
 } lora_plan_stats;
 
 /* Plan for up to max_tokens tokens (device buffers allocated once; on 16-bit
- * pools about 4.1 KB per token for the fused V rows and tile counters, plus a
- * split-K workspace of 64 KB per block and slice grown at first use).  A plan
- * is used by one stream at a time: launches that use the same plan must not
- * overlap (they share its counters and workspaces). */
+ * pools the MFMA tiles' shrink also needs a workspace of partial tiles, about
+ * 4 bytes per token and rank unit per slice of a launch plus the tile
+ * boundaries, grown at first use).  A plan is used by one stream at a time:
+ * launches that use the same plan must not overlap (they share its
+ * workspace). */
 lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** out);
 lora_status lora_plan_destroy(lora_plan* plan);
 /* Build the plan of one batch from host ids [n] (any order, -1 = no adapter):
@@ -205,11 +206,6 @@ lora_status lora_plan_get_stats(const lora_plan* plan, lora_plan_stats* out);
  * and items [n_items][4] = {adapter, start in perm, count, kind (0 short,
  * 1 MFMA tile)}.  Either pointer may be NULL. */
 lora_status lora_plan_export(const lora_plan* plan, int32_t* perm_host, int32_t* items_host);
-/* Number of bounded in-kernel waits (lora_apply on MFMA tiles waits for the V
- * tiles other blocks produce) that gave up instead of finishing; nonzero means
- * the outputs of those launches are invalid.  Blocks until all device work is
- * done (it synchronizes the device). */
-lora_status lora_plan_check(const lora_plan* plan, int32_t* n_timeouts);
 
 /* Shrink for a planned batch: v[i][.] as lora_bgmv_shrink (rows indexed by the
  * original token index). */
@@ -219,8 +215,10 @@ lora_status lora_sgmv_shrink(lora_pool* pool, const lora_plan* plan, int32_t sli
 lora_status lora_sgmv_expand(lora_pool* pool, const lora_plan* plan, int32_t slice,
                              const float* v_dev, int32_t v_ld, void* y_dev, int32_t y_dtype,
                              void* stream);
-/* Fused shrink + expand for a planned (mixed prefill + decode) batch, one launch
- * for up to LORA_MAX_IO slices; v stays in LDS. */
+/* Fused shrink + expand for a planned (mixed prefill + decode) batch, for up to
+ * LORA_MAX_IO slices; v is never materialized.  Short items: one launch, v in
+ * LDS.  MFMA tiles: two launches on `stream` (shrink ranges keep partial tiles
+ * in the plan's workspace; the expand sums them while loading V). */
 lora_status lora_apply(lora_pool* pool, const lora_plan* plan, int32_t n_io,
                        const lora_io* io_host, int32_t y_dtype, void* stream);
 

@@ -79,7 +79,6 @@ def run_sgmv(sp, batch, slices, y_dtype, mode, l_long=0):
         L.lora_apply(sp.handle, plan, [(s, xs[s], ys[s].view) for s in slices], ydt)
     torch.cuda.synchronize()
     stats = L.lora_plan_get_stats(plan)
-    assert L.lora_plan_check(plan) == 0, "fused launch gave up waiting for a V tile"
     L.lora_plan_destroy(plan)
     return {s: ys[s].host() for s in slices}, stats
 
@@ -280,8 +279,8 @@ def test_sgmv_exact_small_bit_exact(mode):
 
 
 def test_sgmv_plan_reuse_repeated_launches():
-    # one plan, several launches in a row: fused (launch epochs), split (stage
-    # counters reset by the reducing block), fused again -- all bit-identical
+    # one plan, several launches in a row (fused, split, fused: the workspace of
+    # partial tiles is reused) -- all bit-identical
     dtype, d_in, d_out, ranks, P, ids = SMALL_SGMV[0]
     log("[case] sgmv plan reuse")
     wl = W.small_workload(dtype, d_in, d_out, ranks, P, n_slices=2, seed=40)
@@ -307,7 +306,6 @@ def test_sgmv_plan_reuse_repeated_launches():
                 L.lora_apply(sp.handle, plan, [(s, xs[s], ys[s].view) for s in range(2)], ydt)
             torch.cuda.synchronize()
             outs.append([ys[s].host() for s in range(2)])
-        assert L.lora_plan_check(plan) == 0
     finally:
         L.lora_plan_destroy(plan)
     for s in range(2):
