@@ -1,11 +1,17 @@
 """Throughput of the heterogeneous-adapter LoRA apply on one MI355X.
 
-Workload: Llama-7B decode BGMV -- 64 tokens (one per request), the q/k/v/o
-projections (4096 -> 4096) of one layer, 1000 rank-16 fp16 adapters scattered
-over a unified page pool.  A step applies every token's adapter to all four
-projections: y_i += s_a B_a (A_a x_i), shrink and expand fused in one launch
-(lora_bgmv_apply).  16 different id batches (with their own x and y buffers)
-rotate, so adapter pages come from HBM rather than the 256 MB Infinity Cache.
+Default workload: Llama-7B decode BGMV -- 64 tokens (one per request), the
+q/k/v/o projections (4096 -> 4096) of one layer, 1000 rank-16 fp16 adapters
+scattered over a unified page pool.  A step applies every token's adapter to
+all four projections: y_i += s_a B_a (A_a x_i), shrink and expand fused in one
+launch (lora_bgmv_apply).  16 different id batches (with their own x and y
+buffers) rotate, so adapter pages come from HBM rather than the 256 MB
+Infinity Cache.
+
+`--workload` runs one of the other synthetic workloads the same way (for
+profiling; the default is the measured configuration): the heterogeneous
+decode batch (lora_bgmv_apply over its two slices) or a planned batch
+(lora_apply over all slices; plans are built before the timed region).
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -41,15 +47,21 @@ def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int) -> int:
     return total
 
 
+# The sources the decode kernel (k_bgmv_apply) is compiled from.
+DECODE_SOURCES = ("k_bgmv.hip", "kcommon.h", "kvalu.h", "lora_internal.h")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources, so counter figures taken on other code are dropped."""
+    """Hash of the decode kernel's sources, so counter figures taken on other
+    code are dropped."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gather_lora_matmul_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+    paths = [os.path.join(csrc, f) for f in DECODE_SOURCES]
+    paths.append(os.path.join(ROOT, "include", "lora_mi355x.h"))
+    for path in paths:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -88,7 +100,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=["fused", "split"], default="fused")
-    ap.add_argument("--batches", type=int, default=16)
+    ap.add_argument("--workload", default="llama7b_decode_bgmv",
+                    choices=["llama7b_decode_bgmv", "hetero_decode_bgmv", "llama13b_prefill_sgmv",
+                             "llama70b_mixed_apply"])
+    ap.add_argument("--batches", type=int, default=None,
+                    help="rotating batches (default 16 for decode, 4 for planned batches)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 64 MiB device copy 10x (HBM counter calibration)")
@@ -105,25 +121,42 @@ def main():
     from gather_lora_matmul_amd.synthetic import SyntheticPool, to_device
 
     torch.cuda.set_device(0)
-    wl = W.make_workload(1)
-    slices = [0, 1, 2, 3]
+    cfg = {"llama7b_decode_bgmv": 1, "hetero_decode_bgmv": 2, "llama13b_prefill_sgmv": 3,
+           "llama70b_mixed_apply": 4}[args.workload]
+    wl = W.make_workload(cfg)
+    planned = cfg >= 3
+    slices = list(range(len(wl.slices)))
+    n_batches = args.batches or (4 if planned else 16)
     print("[bench] building pool: %s, %d adapters x %d slices" % (wl.name, wl.n_adapters, len(slices)),
           file=sys.stderr, flush=True)
     sp = SyntheticPool(wl)
-    batches = [W.make_batch(wl, i) for i in range(args.batches)]
+    batches = [W.make_batch(wl, i) for i in range(n_batches)]
     ids_d = [torch.from_numpy(b.ids).cuda() for b in batches]
     xs = [[to_device(b.x[s], wl.dtype) for s in slices] for b in batches]
     ys = [[to_device(b.y0[s], wl.dtype) for s in slices] for b in batches]
     ydt = W.DTYPE_CODE[wl.dtype]
     n = len(batches[0].ids)
     v = [torch.zeros((n, sp.max_rank), dtype=torch.float32, device="cuda") for _ in slices]
+    plans = []
+    if planned:
+        for b in batches:
+            p = L.lora_plan_create(sp.handle, len(b.ids))
+            L.lora_plan_build(p, b.ids)
+            plans.append(p)
     stream = torch.cuda.current_stream()
 
     def step(i):
         k = i % len(batches)
-        if args.mode == "fused":
-            L.lora_bgmv_apply(sp.handle, [(s, xs[k][j], ys[k][j]) for j, s in enumerate(slices)],
-                              ids_d[k], ydt, stream=stream)
+        io = [(s, xs[k][j], ys[k][j]) for j, s in enumerate(slices)]
+        if planned:
+            if args.mode == "fused":
+                L.lora_apply(sp.handle, plans[k], io, ydt, stream=stream)
+            else:
+                for j, s in enumerate(slices):
+                    L.lora_sgmv_shrink(sp.handle, plans[k], s, xs[k][j], v[j], stream=stream)
+                    L.lora_sgmv_expand(sp.handle, plans[k], s, v[j], ys[k][j], ydt, stream=stream)
+        elif args.mode == "fused":
+            L.lora_bgmv_apply(sp.handle, io, ids_d[k], ydt, stream=stream)
         else:
             for j, s in enumerate(slices):
                 L.lora_bgmv_shrink(sp.handle, s, xs[k][j], ids_d[k], v[j], stream=stream)
@@ -154,7 +187,7 @@ def main():
     avg_bytes = float(np.mean(used))
     avg_kernel_s = float(np.mean(kern_ms)) * 1e-3
     achieved = avg_bytes / avg_kernel_s / 1e9
-    traffic = measured_traffic() if args.mode == "fused" else None
+    traffic = measured_traffic() if args.mode == "fused" and cfg == 1 else None
     if args.copy_calib:
         src = torch.empty(64 << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -172,12 +205,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": "llama7b_decode_bgmv", "tokens_per_step": n,
-                   "slices": "q,k,v,o 4096x4096", "adapters": wl.n_adapters, "rank": 16,
-                   "weights": "fp16 N(0,0.02), pages scattered", "entry":
-                   "lora_bgmv_apply" if args.mode == "fused" else "lora_bgmv_shrink+expand",
+        "config": {"workload": wl.name, "tokens_per_step": n,
+                   "slices": ", ".join("%dx%d" % tuple(d) for d in wl.slices),
+                   "adapters": wl.n_adapters,
+                   "rank": sorted(set(int(r) for r in wl.ranks)) if cfg != 1 else 16,
+                   "weights": "%s N(0,0.02), pages scattered" % wl.dtype,
+                   "entry": ("lora_apply" if planned else "lora_bgmv_apply") if args.mode == "fused"
+                   else ("lora_sgmv_shrink+expand" if planned else "lora_bgmv_shrink+expand"),
                    "id_batches_rotated": len(batches)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
@@ -188,7 +224,10 @@ def main():
     }
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
-        out["cpu_baseline"] = cpu_baseline(wl, batches[:4], slices, threads)
+        out["cpu_baseline"] = cpu_baseline(wl, batches[:4] if cfg <= 2 else batches[:1], slices,
+                                           threads)
+    for p in plans:
+        L.lora_plan_destroy(p)
     sp.close()
     print(json.dumps(out), flush=True)
 
