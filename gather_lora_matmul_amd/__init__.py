@@ -69,6 +69,14 @@ class PlanStats(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError("liblora_mi355x.so is not built: run `python gather_lora_matmul_amd/build.py`")
+    # One HIP runtime per process: torch ships its own libamdhip64 (same soname
+    # as ROCm's), and of two runtimes in one process only the first to start
+    # sees the GPU.  With torch loaded first, this library binds to its runtime
+    # and shares device pointers and streams with it.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     V, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     sig = {

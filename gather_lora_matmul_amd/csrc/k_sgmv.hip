@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kMT, 2) void k_sgmv_expand_tiles(PoolView pv, PlanV
   __shared__ __attribute__((aligned(16))) char bb[kVpB];
   __shared__ __attribute__((aligned(16))) char bc[kDsB];
   const int L = logical_block(blockIdx.x, pl.G);
-  expand_range<T, TY>(pv, pl, io, 0, L, v, v_ld, LdsBufs{misc, ba, bb, bc});
+  expand_range<T, TY, false>(pv, pl, io, 0, L, v, v_ld, LdsBufs{misc, ba, bb, bc});
 }
 
 // Fused apply on MFMA tiles: two launches on one stream.  The first runs every
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kMT, 2) void k_apply_expand_tiles(PoolView pv, Plan
   __shared__ __attribute__((aligned(16))) char bc[kDsB];
   const int L = logical_block(blockIdx.x, pl.G);
   const LdsBufs lb{misc, ba, bb, bc};
-  for (int j = 0; j < ios.n_io; ++j) expand_range<T, TY>(pv, pl, ios.io[j], j, L, nullptr, 0, lb);
+  for (int j = 0; j < ios.n_io; ++j) expand_range<T, TY, true>(pv, pl, ios.io[j], j, L, nullptr, 0, lb);
 }
 
 // ---- launchers ------------------------------------------------------------------

@@ -240,25 +240,26 @@ __device__ __forceinline__ void shrink_stages(const PoolView& pv, const DevEntry
     }
   };
   // Three-buffer ring: stages s + 1 and s + 2 are in flight while stage s is
-  // computed.  Each step waits for the wave's own loads of stage s (the two
-  // later stages stay outstanding); the barrier then makes every wave's loads
-  // of stage s visible and frees the buffer of stage s - 1 for stage s + 2.
-  // Past s1 - 1 the issues repeat the last stage (never computed).
+  // computed.  Each step waits for the wave's own loads of stage s (stage s + 1,
+  // if there is one, stays outstanding); the barrier then makes every wave's
+  // loads of stage s visible and frees the buffer of stage s - 1 for stage
+  // s + 2.  No stage past s1 - 1 is issued, so no load is in flight when the
+  // range ends.  (The conditions are block-uniform.)
   auto step = [&](int s, const char* cur, char* nxt2) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(LPS));
+    if (s + 1 < s1) __builtin_amdgcn_s_waitcnt(wait_vm(LPS));
+    else __builtin_amdgcn_s_waitcnt(wait_vm(0));
     lds_barrier();
-    issue(min(s + 2, s1 - 1), nxt2);
+    if (s + 2 < s1) issue(s + 2, nxt2);
     compute(s, cur);
   };
   issue(s0, lb.a);
-  issue(min(s0 + 1, s1 - 1), lb.b);
+  if (s0 + 1 < s1) issue(s0 + 1, lb.b);
   for (int s = s0; s < s1; s += 3) {
     step(s, lb.a, lb.c);
     if (s + 1 < s1) step(s + 1, lb.b, lb.a);
     if (s + 2 < s1) step(s + 2, lb.c, lb.b);
   }
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no load may land after the range
-  __syncthreads();
+  lds_barrier();  // every wave is done with the stage buffers
 }
 
 // ---- shrink outputs ---------------------------------------------------------------
@@ -339,7 +340,7 @@ __device__ __forceinline__ void shrink_tile(const PoolView& pv, const PlanView& 
         part[(nb * ntb + w) * 64 + lane] = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
     }
   }
-  __syncthreads();
+  lds_barrier();  // the tile's tokens in LDS are free (the stores stay in flight)
 }
 
 // The block's shrink range in launch slice j.
@@ -468,12 +469,14 @@ __device__ __forceinline__ void load_v_tile(const float* v, int v_ld, const int*
   }
 }
 
-// Chunks [c0, c1) (64 output rows each) of one tile; V packed in LDS.
-template <typename T, typename TY, int NK>
+// Chunks [c0, c1) (64 output rows each) of one tile.  `load_v` packs the
+// tile's V into LDS (Vh, Vl); it runs while the loads of the first two chunks
+// are in flight, so their latencies overlap.
+template <typename T, typename TY, int NK, typename LoadV>
 __device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry& e,
                                               const IoDesc& io, const int* toks, int count,
                                               int c0, int c1, const uint16_t* Vh,
-                                              const uint16_t* Vl, float* D) {
+                                              const uint16_t* Vl, float* D, LoadV&& load_v) {
   typedef typename MfmaOp<T>::vec vec;
   constexpr int EPP = YPiece<TY>::EPP;
   constexpr int PPR = 64 / EPP;              // pieces per token row of a chunk
@@ -575,6 +578,8 @@ __device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry
   loadB(min(c0 + 1, c1 - 1), b1);
   loadY(min(c0 + 1, c1 - 1), y1);
   __builtin_amdgcn_sched_barrier(0);
+  load_v();
+  lds_barrier();  // V is in LDS
   for (int c = c0; c < c1; c += 3) {
     loadB(min(c + 2, c1 - 1), b2);
     loadY(min(c + 2, c1 - 1), y2);
@@ -590,35 +595,47 @@ __device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry
 
 // Fused: V of a tile from its contributors' partial tiles (summed in block
 // order, as the split API's reduce does) -> hi and lo parts in LDS.  Columns
-// [16 * ceil(rank / 16), 32 * NK) and slots past the count are zero.  Each
-// thread owns at most 8 units; a contributor's units are loaded together.
+// [16 * ceil(rank / 16), 32 * NK) and slots past the count are zero.  A tile
+// has at most 2 NK rank blocks of 4 token blocks, so each thread owns at most
+// UPT = 2 NK float4 units of a partial tile; the loads of CG contributors are
+// issued together (clamped to the last contributor, whose repeats are not
+// added).
 template <typename T, int NK>
 __device__ __forceinline__ void load_v_parts(const PlanView& pl, int j, const int32_t* lst, int c0,
                                              int c1, int count, int rank, uint16_t* Vh,
                                              uint16_t* Vl) {
   constexpr int KW = 32 * NK;
+  constexpr int UPT = 2 * NK;
+  constexpr int CG = UPT >= 8 ? 1 : 8 / UPT;
   const int ntb = (count + 15) >> 4;
-  const int nu = ((rank + 15) >> 4) * ntb * 64;  // <= 8 * 4 * 64
-  float4 sum[8];
-  for (int c = c0; c < c1; ++c) {
-    const float4* src = part_at(pl, j, lst[2 * c + 1]);
-    float4 q[8];
+  const int nu = ((rank + 15) >> 4) * ntb * 64;  // <= UPT * kMT
+  float4 sum[UPT];
+  for (int c = c0; c < c1; c += CG) {
+    float4 q[CG][UPT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = src[min((int)threadIdx.x + kMT * i, nu - 1)];
+    for (int g = 0; g < CG; ++g) {
+      const float4* src = part_at(pl, j, lst[2 * min(c + g, c1 - 1) + 1]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (c == c0) {
-        sum[i] = q[i];
-      } else {
-        sum[i].x += q[i].x;
-        sum[i].y += q[i].y;
-        sum[i].z += q[i].z;
-        sum[i].w += q[i].w;
+      for (int i = 0; i < UPT; ++i) q[g][i] = src[min((int)threadIdx.x + kMT * i, nu - 1)];
+    }
+#pragma unroll
+    for (int g = 0; g < CG; ++g) {
+      if (c + g >= c1) break;
+#pragma unroll
+      for (int i = 0; i < UPT; ++i) {
+        if (c + g == c0) {
+          sum[i] = q[g][i];
+        } else {
+          sum[i].x += q[g][i].x;
+          sum[i].y += q[g][i].y;
+          sum[i].z += q[g][i].z;
+          sum[i].w += q[g][i].w;
+        }
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < UPT; ++i) {
     const int u = threadIdx.x + kMT * i;
     if (u < nu) {
       const int sl = unit_slot(u, ntb);
@@ -646,9 +663,9 @@ __device__ __forceinline__ void load_v_parts(const PlanView& pl, int j, const in
 }
 
 // The block's expand range in launch slice j.  Split API: V from the caller's
-// v (rows by token).  Fused (v == null): V of a tile from its partial tiles,
-// written by the shrink launch that precedes this one on the stream.
-template <typename T, typename TY>
+// v (rows by token).  Fused (kFused, v unused): V of a tile from its partial
+// tiles, written by the shrink launch that precedes this one on the stream.
+template <typename T, typename TY, bool kFused>
 __device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView& pl,
                                              const IoDesc& io, int j, int L, const float* v,
                                              int v_ld, const LdsBufs& lb) {
@@ -672,31 +689,31 @@ __device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView&
     __syncthreads();
     switch ((e.rs + 31) >> 5) {
       case 1:
-        if (v) load_v_tile<T, 1>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
-        else load_v_parts<T, 1>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
-        __syncthreads();
-        expand_chunks<T, TY, 1>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
+        expand_chunks<T, TY, 1>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
+          if constexpr (kFused) load_v_parts<T, 1>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+          else load_v_tile<T, 1>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
+        });
         break;
       case 2:
-        if (v) load_v_tile<T, 2>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
-        else load_v_parts<T, 2>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
-        __syncthreads();
-        expand_chunks<T, TY, 2>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
+        expand_chunks<T, TY, 2>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
+          if constexpr (kFused) load_v_parts<T, 2>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+          else load_v_tile<T, 2>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
+        });
         break;
       case 3:
-        if (v) load_v_tile<T, 3>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
-        else load_v_parts<T, 3>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
-        __syncthreads();
-        expand_chunks<T, TY, 3>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
+        expand_chunks<T, TY, 3>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
+          if constexpr (kFused) load_v_parts<T, 3>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+          else load_v_tile<T, 3>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
+        });
         break;
       default:
-        if (v) load_v_tile<T, 4>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
-        else load_v_parts<T, 4>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
-        __syncthreads();
-        expand_chunks<T, TY, 4>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds);
+        expand_chunks<T, TY, 4>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
+          if constexpr (kFused) load_v_parts<T, 4>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+          else load_v_tile<T, 4>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
+        });
         break;
     }
-    __syncthreads();
+    lds_barrier();  // tokens and V are free (the y stores stay in flight)
   }
 }
 
