@@ -59,6 +59,18 @@ lora_status build_ioset(const lora_pool* p, int32_t n_io, const lora_io* io, IoS
   return LORA_OK;
 }
 
+// A launch of one slice (split API): its layout has the same key as a fused
+// launch of that slice alone.
+IoSet single_io(const IoDesc& io) {
+  IoSet s;
+  memset(&s, 0, sizeof(s));
+  s.n_io = 1;
+  s.io[0] = io;
+  s.max_d_in = io.d_in;
+  s.max_d_out = io.d_out;
+  return s;
+}
+
 }  // namespace
 
 #define LORA_TRY(expr)          \
@@ -125,9 +137,10 @@ lora_status lora_sgmv_shrink(lora_pool* p, const lora_plan* pl, int32_t slice, c
   if (!x || !v) return fail(LORA_E_ARG, "null device pointer");
   if (!aligned16(x)) return fail(LORA_E_ARG, "x not 16-byte aligned");
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
-  if (pl->n_mfma > 0) LORA_TRY(plan_reserve_part(const_cast<lora_plan*>(pl), 1));
-  return hip_status(launch_sgmv_shrink(p->dtype, p->view(), pl->view(), p->io(slice, x, nullptr), v,
-                                       v_ld, (hipStream_t)stream),
+  const IoDesc io = p->io(slice, x, nullptr);
+  const PlanLayout* lay = nullptr;
+  if (pl->n_mfma > 0) LORA_TRY(plan_layout(const_cast<lora_plan*>(pl), single_io(io), (hipStream_t)stream, &lay));
+  return hip_status(launch_sgmv_shrink(p->dtype, p->view(), pl->view(lay), io, v, v_ld, (hipStream_t)stream),
                     "sgmv_shrink");
 }
 
@@ -142,8 +155,11 @@ lora_status lora_sgmv_expand(lora_pool* p, const lora_plan* pl, int32_t slice, c
   if (!v || !y) return fail(LORA_E_ARG, "null device pointer");
   if (!aligned16(y)) return fail(LORA_E_ARG, "y not 16-byte aligned");
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
-  return hip_status(launch_sgmv_expand(p->dtype, y_dtype, p->view(), pl->view(),
-                                       p->io(slice, nullptr, y), v, v_ld, (hipStream_t)stream),
+  const IoDesc io = p->io(slice, nullptr, y);
+  const PlanLayout* lay = nullptr;
+  if (pl->n_mfma > 0) LORA_TRY(plan_layout(const_cast<lora_plan*>(pl), single_io(io), (hipStream_t)stream, &lay));
+  return hip_status(launch_sgmv_expand(p->dtype, y_dtype, p->view(), pl->view(lay), io, v, v_ld,
+                                       (hipStream_t)stream),
                     "sgmv_expand");
 }
 
@@ -156,8 +172,9 @@ lora_status lora_apply(lora_pool* p, const lora_plan* pl, int32_t n_io, const lo
   IoSet ios;
   LORA_TRY(build_ioset(p, n_io, io, ios));
   if (pl->n_tokens == 0) return LORA_OK;
-  if (pl->n_mfma > 0) LORA_TRY(plan_reserve_part(const_cast<lora_plan*>(pl), n_io));
-  return hip_status(launch_apply(p->dtype, y_dtype, p->view(), pl->view(), ios, (hipStream_t)stream),
+  const PlanLayout* lay = nullptr;
+  if (pl->n_mfma > 0) LORA_TRY(plan_layout(const_cast<lora_plan*>(pl), ios, (hipStream_t)stream, &lay));
+  return hip_status(launch_apply(p->dtype, y_dtype, p->view(), pl->view(lay), ios, (hipStream_t)stream),
                     "apply");
 }
 

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kMT, 2) void k_sgmv_shrink_tiles(PoolView pv, PlanV
   __shared__ __attribute__((aligned(16))) char bb[kBufB];
   __shared__ __attribute__((aligned(16))) char bc[kBufB];
   const int L = logical_block(blockIdx.x, pl.G);
-  shrink_range<T>(pv, pl, io, 0, L, v, v_ld, LdsBufs{misc, ba, bb, bc});
+  shrink_range<T>(pv, pl, [&](int) -> const IoDesc& { return io; }, L, v, v_ld, LdsBufs{misc, ba, bb, bc});
 }
 
 // Split API: v rows of the tiles whose shrink several blocks shared (block = tile).
@@ -169,13 +169,15 @@ __global__ __launch_bounds__(kMT, 2) void k_sgmv_expand_tiles(PoolView pv, PlanV
   __shared__ __attribute__((aligned(16))) char bb[kVpB];
   __shared__ __attribute__((aligned(16))) char bc[kDsB];
   const int L = logical_block(blockIdx.x, pl.G);
-  expand_range<T, TY, false>(pv, pl, io, 0, L, v, v_ld, LdsBufs{misc, ba, bb, bc});
+  expand_range<T, TY, false>(pv, pl, [&](int) -> const IoDesc& { return io; }, L, v, v_ld,
+                            LdsBufs{misc, ba, bb, bc});
 }
 
 // Fused apply on MFMA tiles: two launches on one stream.  The first runs every
-// block's shrink range of every slice and keeps each contribution as a partial
-// tile; the second runs the expand ranges, V of a tile being the sum of its
-// partial tiles (block order).  v itself is never materialized.
+// block's shrink range (over the launch slices in order) and keeps each
+// contribution as a partial tile; the second runs the expand ranges, V of a
+// tile being the sum of its partial tiles (block order).  v itself is never
+// materialized.
 template <typename T>
 __global__ __launch_bounds__(kMT, 2) void k_apply_shrink_tiles(PoolView pv, PlanView pl, IoSet ios) {
   __shared__ __attribute__((aligned(16))) char misc[kMiscB];
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(kMT, 2) void k_apply_shrink_tiles(PoolView pv, Plan
   __shared__ __attribute__((aligned(16))) char bc[kBufB];
   const int L = logical_block(blockIdx.x, pl.G);
   const LdsBufs lb{misc, ba, bb, bc};
-  for (int j = 0; j < ios.n_io; ++j) shrink_range<T>(pv, pl, ios.io[j], j, L, nullptr, 0, lb);
+  shrink_range<T>(pv, pl, [&](int j) -> const IoDesc& { return ios.io[j]; }, L, nullptr, 0, lb);
 }
 
 template <typename T, typename TY>
@@ -195,7 +197,8 @@ __global__ __launch_bounds__(kMT, 2) void k_apply_expand_tiles(PoolView pv, Plan
   __shared__ __attribute__((aligned(16))) char bc[kDsB];
   const int L = logical_block(blockIdx.x, pl.G);
   const LdsBufs lb{misc, ba, bb, bc};
-  for (int j = 0; j < ios.n_io; ++j) expand_range<T, TY, true>(pv, pl, ios.io[j], j, L, nullptr, 0, lb);
+  expand_range<T, TY, true>(pv, pl, [&](int j) -> const IoDesc& { return ios.io[j]; }, L, nullptr, 0,
+                            lb);
 }
 
 // ---- launchers ------------------------------------------------------------------

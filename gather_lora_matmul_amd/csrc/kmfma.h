@@ -2,19 +2,21 @@
 // segments of the multi-LoRA serving article, SGMV section).
 //
 // A tile is up to 64 token slots of one group; blocks of four waves run
-// v_mfma_f32_16x16x32_{bf16,f16}.  The kernels are persistent: the planner
-// splits the tiles, weighted by the bytes they move, into one contiguous range
-// per block (BlockStart tables), so every block moves about the same number of
-// bytes and no block waits in a second round.
+// v_mfma_f32_16x16x32_{bf16,f16}.  The kernels are persistent: for each launch
+// shape the host splits the launch's work sequence (the tiles of launch slice
+// 0, then of slice 1, ...; stages or chunks weighted by the bytes they move)
+// into one contiguous range per block (layout.h), so every block moves about
+// the same number of bytes and no block waits in a second round.
 //
 // Shrink  V^T[n][t] = sum_j A[n][j] X[t][j]   (M = rank, N = tokens, K = d_in)
-//   Stages of 64 columns: the block loads the X rows of the tile's tokens and
-//   the A rows of the adapter with coalesced 16-byte loads (eight lanes per
-//   128-byte row segment) into registers two stages ahead, stores them to LDS
-//   and the waves read their MFMA operands from there; wave w owns tokens
-//   [16w, 16w + 16) and all rank blocks.  A block whose range covers only part
-//   of a tile's stages writes a partial tile; the block that completes the
-//   tile's stage count sums the partials in block order (deterministic).
+//   Stages of 64 columns: the X rows of the tile's tokens and the A rows of
+//   the adapter go from global memory straight into LDS (16-byte loads, eight
+//   lanes per 128-byte row segment) through a three-buffer ring, two stages
+//   in flight while one is computed; wave w owns tokens [16w, 16w + 16) and
+//   all rank blocks.  A range may cover only part of a tile's stages (split
+//   K); each such contribution is a partial tile.  Split API: a block that
+//   covers a whole tile writes v, a reduce kernel sums the partials of the
+//   others in block order; fused apply: the expand sums them while loading V.
 // Expand  Y^T[m][t] += s * sum_k B[m][k] V[t][k]  (M = output rows, N = tokens,
 //   K = rank), in chunks of 64 rows: wave w computes rows [16w, 16w + 16) of
 //   the chunk for all tokens; B rows are read from their pages in natural
@@ -119,23 +121,41 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---- block ranges -----------------------------------------------------------------
-struct Pos {
-  int tile;
-  int k;
-};
-__device__ __forceinline__ bool pos_lt(Pos a, int tile, int k) {
-  return a.tile < tile || (a.tile == tile && a.k < k);
-}
-// First unit (tile, stage or chunk) of logical block L in a slice whose tiles
-// have n units each.  L is block-uniform: the table entry is a scalar load.
-__device__ __forceinline__ Pos range_start(const BlockStart* bs, int L, int n, int n_tiles) {
+// Block L's range is [pos[L], pos[L + 1]) of the launch's work sequence (the
+// tiles of launch slice 0, then of slice 1, ...).  L is block-uniform: the
+// table entries are scalar loads.
+__device__ __forceinline__ RangePos load_pos(const RangePos* tab, int L) {
   typedef const __attribute__((address_space(4))) int32_t* cptr;
-  const cptr p = (cptr)(bs + L);
-  const int tile = p[0], off = p[1], w = p[2];
-  if (tile >= n_tiles) return Pos{n_tiles, 0};
-  const int k = (int)(((uint32_t)n * (uint32_t)off + (uint32_t)w - 1u) / (uint32_t)w);  // n*off < 2^27
-  if (k >= n) return Pos{tile + 1, 0};
-  return Pos{tile, k};
+  const cptr p = (cptr)(tab + L);
+  return RangePos{p[0], p[1], p[2], 0};
+}
+__device__ __forceinline__ bool pos_before(int j, int t, int k, const RangePos& b) {
+  return j < b.j || (j == b.j && (t < b.tile || (t == b.tile && k < b.k)));
+}
+// fn(j, tile, k0, k1, first, last) for every piece of block L's range, in
+// order: units [k0, k1) of `tile` in launch slice j (units(j) per tile),
+// first / last: the piece is the range's first / last one.
+template <typename Units, typename Fn>
+__device__ __forceinline__ void for_each_piece(const RangePos* tab, int L, int n_tiles,
+                                               Units&& units, Fn&& fn) {
+  const RangePos a = load_pos(tab, L);
+  const RangePos b = load_pos(tab, L + 1);
+  int j = a.j, t = a.tile, k = a.k;
+  bool first = true;
+  while (pos_before(j, t, k, b)) {
+    const bool ends_here = j == b.j && t == b.tile;
+    const int k1 = ends_here ? b.k : units(j);
+    int nj = j, nt = t + 1;
+    if (nt == n_tiles) {
+      nt = 0;
+      ++nj;
+    }
+    fn(j, t, k, k1, first, ends_here || !pos_before(nj, nt, 0, b));
+    first = false;
+    j = nj;
+    t = nt;
+    k = 0;
+  }
 }
 // Blocks are dealt round-robin to the 8 XCDs; logical blocks [x*G/8, (x+1)*G/8)
 // run on XCD x, so neighbouring ranges (the same adapters) share an L2.
@@ -265,14 +285,14 @@ __device__ __forceinline__ void shrink_stages(const PoolView& pv, const DevEntry
 // ---- shrink outputs ---------------------------------------------------------------
 // A block's contribution to a tile is a partial tile in the MFMA lane layout:
 // float4 unit (nb * ntb + w) * 64 + lane holds ranks 16 nb + 4 g + [0, 4) of
-// slot 16 w + r16 (ntb = token blocks of the tile).  Contribution c of a tile
-// (its entry in the slice's list) sits at its listed offset in the launch
-// slice's region.
-__device__ __forceinline__ const int32_t* contrib_list(const PlanView& pl, int slice) {
-  return pl.contrib + (int64_t)slice * 2 * pl.contrib_cap;
+// slot 16 w + r16 (ntb = token blocks of the tile), at the contribution's
+// float4 offset in the plan's partial-tile workspace.
+__device__ __forceinline__ float4* part_at(const PlanView& pl, int32_t off) {
+  return reinterpret_cast<float4*>(pl.part) + off;
 }
-__device__ __forceinline__ float4* part_at(const PlanView& pl, int j, int32_t off) {
-  return reinterpret_cast<float4*>(pl.part) + (int64_t)j * pl.part_stride + off;
+// Contributions [c_off[0], c_off[1]) of tile i in launch slice j.
+__device__ __forceinline__ const int32_t* contrib_range(const PlanView& pl, int j, int i) {
+  return pl.c_off + (int64_t)j * (pl.n_mfma + 1) + i;
 }
 // Unit u of a partial tile with ntb token blocks -> (slot, first rank)
 __device__ __forceinline__ int unit_slot(int u, int ntb) { return 16 * ((u >> 6) % ntb) + (u & 15); }
@@ -296,16 +316,16 @@ __device__ __forceinline__ void v_zero_tail(float* v, int v_ld, const int* toks,
   }
 }
 
-// One tile of the block's shrink range: stages [k0, k1) of nst.  Split API
-// (v != null): a block that covers the whole tile writes v; others write their
-// partial tile, summed by the reduce kernel.  Fused (v == null): every
-// contribution is a partial tile, summed when the expand loads V.
+// One piece of the block's shrink range: stages [k0, k1) of nst of a tile.
+// Split API (v != null): a block that covers the whole tile writes v; others
+// write their partial tile (at float4 offset part_off), summed by the reduce
+// kernel.  Fused (v == null): every contribution is a partial tile, summed
+// when the expand loads V.
 template <typename T, int NB>
 __device__ __forceinline__ void shrink_tile(const PoolView& pv, const PlanView& pl,
-                                            const DevEntry& e, const IoDesc& io, int j, int L,
-                                            int tile, int count, int k0, int k1, int nst,
-                                            bool first_of_range, float* v, int v_ld,
-                                            const LdsBufs& lb) {
+                                            const DevEntry& e, const IoDesc& io, int count,
+                                            int k0, int k1, int nst, int32_t part_off, float* v,
+                                            int v_ld, const LdsBufs& lb) {
   const int* toks = reinterpret_cast<const int*>(lb.misc + kOffToks);
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -327,13 +347,7 @@ __device__ __forceinline__ void shrink_tile(const PoolView& pv, const PlanView& 
     }
     v_zero_tail(v, v_ld, toks, count, 16 * NB);
   } else {
-    // this contribution's entry in the tile's list (block-uniform scalar loads)
-    const int entry = (L << 1) | (first_of_range ? 0 : 1);
-    const int32_t* lst = contrib_list(pl, io.slice);
-    const int32_t* off = pl.contrib_off + io.slice * (pl.tile_cap + 1);
-    int c = off[tile];
-    while (c < off[tile + 1] - 1 && lst[2 * c] != entry) ++c;
-    float4* part = part_at(pl, j, lst[2 * c + 1]);
+    float4* part = part_at(pl, part_off);
     if (w < ntb) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -343,21 +357,23 @@ __device__ __forceinline__ void shrink_tile(const PoolView& pv, const PlanView& 
   lds_barrier();  // the tile's tokens in LDS are free (the stores stay in flight)
 }
 
-// The block's shrink range in launch slice j.
-template <typename T>
-__device__ __forceinline__ void shrink_range(const PoolView& pv, const PlanView& pl,
-                                             const IoDesc& io, int j, int L, float* v, int v_ld,
-                                             const LdsBufs& lb) {
-  const int nst = (io.d_in + kKC - 1) / kKC;
-  const Pos a = range_start(pl.bs_shrink, L, nst, pl.n_mfma);
-  const Pos b = range_start(pl.bs_shrink, L + 1, nst, pl.n_mfma);
+// The block's shrink range over the launch slices ios[0 .. n_io).  The
+// partial tiles of its first and last piece sit at part_fl[L]; a piece in
+// between covers a whole tile, the tile's only contribution.
+template <typename T, typename IoOf>
+__device__ __forceinline__ void shrink_range(const PoolView& pv, const PlanView& pl, IoOf&& io_of,
+                                             int L, float* v, int v_ld, const LdsBufs& lb) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  const cptr fl = (cptr)(pl.part_fl + L);
+  const int32_t part_first = fl[0], part_last = fl[1];
   int* toks = reinterpret_cast<int*>(lb.misc + kOffToks);
-  for (int i = a.tile; i < pl.n_mfma && pos_lt(Pos{i, 0}, b.tile, b.k); ++i) {
-    const int k0 = i == a.tile ? a.k : 0;
-    const int k1 = i == b.tile ? b.k : nst;
-    if (k0 >= k1) continue;
+  for_each_piece(pl.bs_shrink, L, pl.n_mfma, [&](int j) { return (io_of(j).d_in + kKC - 1) / kKC; },
+                 [&](int j, int i, int k0, int k1, bool first, bool last) {
+    const IoDesc io = io_of(j);
+    const int nst = (io.d_in + kKC - 1) / kKC;
     const PlanItem item = pl.items[i];
     const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
+    const int32_t part_off = first ? part_first : last ? part_last : pl.c_ent[*contrib_range(pl, j, i)];
     load_tile_tokens(pl, item, toks);
     {  // A page ids of the tile's rank rows (rows past the rank repeat the last)
       int* apg = reinterpret_cast<int*>(lb.misc + kOffApg);
@@ -369,27 +385,25 @@ __device__ __forceinline__ void shrink_range(const PoolView& pv, const PlanView&
       }
     }
     __syncthreads();
-    const bool first = i == a.tile;
     switch ((e.rank + 15) >> 4) {
-      case 1: shrink_tile<T, 1>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
-      case 2: shrink_tile<T, 2>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
-      case 3: shrink_tile<T, 3>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
-      case 4: shrink_tile<T, 4>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
-      case 5: shrink_tile<T, 5>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
-      case 6: shrink_tile<T, 6>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
-      case 7: shrink_tile<T, 7>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
-      default: shrink_tile<T, 8>(pv, pl, e, io, j, L, i, item.count, k0, k1, nst, first, v, v_ld, lb); break;
+      case 1: shrink_tile<T, 1>(pv, pl, e, io, item.count, k0, k1, nst, part_off, v, v_ld, lb); break;
+      case 2: shrink_tile<T, 2>(pv, pl, e, io, item.count, k0, k1, nst, part_off, v, v_ld, lb); break;
+      case 3: shrink_tile<T, 3>(pv, pl, e, io, item.count, k0, k1, nst, part_off, v, v_ld, lb); break;
+      case 4: shrink_tile<T, 4>(pv, pl, e, io, item.count, k0, k1, nst, part_off, v, v_ld, lb); break;
+      case 5: shrink_tile<T, 5>(pv, pl, e, io, item.count, k0, k1, nst, part_off, v, v_ld, lb); break;
+      case 6: shrink_tile<T, 6>(pv, pl, e, io, item.count, k0, k1, nst, part_off, v, v_ld, lb); break;
+      case 7: shrink_tile<T, 7>(pv, pl, e, io, item.count, k0, k1, nst, part_off, v, v_ld, lb); break;
+      default: shrink_tile<T, 8>(pv, pl, e, io, item.count, k0, k1, nst, part_off, v, v_ld, lb); break;
     }
-  }
+  });
 }
 
 // Split API: v rows of a tile that several blocks shared: the sum of their
 // partial tiles in block order (the first one, then += the others).
 __device__ __forceinline__ void shrink_reduce_tile(const PlanView& pl, const IoDesc& io, int tile,
                                                    int rank, float* v, int v_ld, int* toks) {
-  const int32_t* off = pl.contrib_off + io.slice * (pl.tile_cap + 1);
-  const int32_t* lst = contrib_list(pl, io.slice);
-  const int c0 = off[tile], c1 = off[tile + 1];
+  const int32_t* off = contrib_range(pl, 0, tile);
+  const int c0 = off[0], c1 = off[1];
   if (c1 - c0 <= 1) return;  // a single block covered the tile and wrote v
   const PlanItem item = pl.items[tile];
   load_tile_tokens(pl, item, toks);
@@ -399,9 +413,9 @@ __device__ __forceinline__ void shrink_reduce_tile(const PlanView& pl, const IoD
   for (int u = threadIdx.x; u < nu; u += kMT) {
     const int sl = unit_slot(u, ntb);
     if (sl >= item.count) continue;
-    float4 sum = part_at(pl, 0, lst[2 * c0 + 1])[u];
+    float4 sum = part_at(pl, pl.c_ent[c0])[u];
     for (int c = c0 + 1; c < c1; ++c) {
-      const float4 q = part_at(pl, 0, lst[2 * c + 1])[u];
+      const float4 q = part_at(pl, pl.c_ent[c])[u];
       sum.x += q.x;
       sum.y += q.y;
       sum.z += q.z;
@@ -601,9 +615,8 @@ __device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry
 // issued together (clamped to the last contributor, whose repeats are not
 // added).
 template <typename T, int NK>
-__device__ __forceinline__ void load_v_parts(const PlanView& pl, int j, const int32_t* lst, int c0,
-                                             int c1, int count, int rank, uint16_t* Vh,
-                                             uint16_t* Vl) {
+__device__ __forceinline__ void load_v_parts(const PlanView& pl, int c0, int c1, int count,
+                                             int rank, uint16_t* Vh, uint16_t* Vl) {
   constexpr int KW = 32 * NK;
   constexpr int UPT = 2 * NK;
   constexpr int CG = UPT >= 8 ? 1 : 8 / UPT;
@@ -614,7 +627,7 @@ __device__ __forceinline__ void load_v_parts(const PlanView& pl, int j, const in
     float4 q[CG][UPT];
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
-      const float4* src = part_at(pl, j, lst[2 * min(c + g, c1 - 1) + 1]);
+      const float4* src = part_at(pl, pl.c_ent[min(c + g, c1 - 1)]);
 #pragma unroll
       for (int i = 0; i < UPT; ++i) q[g][i] = src[min((int)threadIdx.x + kMT * i, nu - 1)];
     }
@@ -662,59 +675,54 @@ __device__ __forceinline__ void load_v_parts(const PlanView& pl, int j, const in
   }
 }
 
-// The block's expand range in launch slice j.  Split API: V from the caller's
-// v (rows by token).  Fused (kFused, v unused): V of a tile from its partial
-// tiles, written by the shrink launch that precedes this one on the stream.
-template <typename T, typename TY, bool kFused>
-__device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView& pl,
-                                             const IoDesc& io, int j, int L, const float* v,
-                                             int v_ld, const LdsBufs& lb) {
-  const int nch = (io.d_out + 63) / 64;
-  const Pos a = range_start(pl.bs_expand, L, nch, pl.n_mfma);
-  const Pos b = range_start(pl.bs_expand, L + 1, nch, pl.n_mfma);
+// The block's expand range over the launch slices ios[0 .. n_io).  Split
+// API: V from the caller's v (rows by token).  Fused (kFused, v unused): V of
+// a tile from its partial tiles, written by the shrink launch that precedes
+// this one on the stream.
+template <typename T, typename TY, bool kFused, typename IoOf>
+__device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView& pl, IoOf&& io_of,
+                                             int L, const float* v, int v_ld, const LdsBufs& lb) {
   int* toks = reinterpret_cast<int*>(lb.misc + kOffToks);
   uint16_t* Vh = reinterpret_cast<uint16_t*>(lb.a);
   uint16_t* Vl = reinterpret_cast<uint16_t*>(lb.b);
   float* Ds = reinterpret_cast<float*>(lb.c);
-  for (int i = a.tile; i < pl.n_mfma && pos_lt(Pos{i, 0}, b.tile, b.k); ++i) {
-    const int c0 = i == a.tile ? a.k : 0;
-    const int c1 = i == b.tile ? b.k : nch;
-    if (c0 >= c1) continue;
+  for_each_piece(pl.bs_expand, L, pl.n_mfma, [&](int j) { return (io_of(j).d_out + 63) / 64; },
+                 [&](int j, int i, int c0, int c1, bool, bool) {
+    const IoDesc io = io_of(j);
     const PlanItem item = pl.items[i];
     const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
     load_tile_tokens(pl, item, toks);
-    const int32_t* off = pl.contrib_off + io.slice * (pl.tile_cap + 1);
-    const int32_t* lst = contrib_list(pl, io.slice);
-    const int cb0 = off[i], cb1 = off[i + 1];
+    const int32_t* off = contrib_range(pl, j, i);
+    const int cb0 = off[0], cb1 = off[1];
     __syncthreads();
     switch ((e.rs + 31) >> 5) {
       case 1:
         expand_chunks<T, TY, 1>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
-          if constexpr (kFused) load_v_parts<T, 1>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+          if constexpr (kFused) load_v_parts<T, 1>(pl, cb0, cb1, item.count, e.rank, Vh, Vl);
           else load_v_tile<T, 1>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
         });
         break;
       case 2:
         expand_chunks<T, TY, 2>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
-          if constexpr (kFused) load_v_parts<T, 2>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+          if constexpr (kFused) load_v_parts<T, 2>(pl, cb0, cb1, item.count, e.rank, Vh, Vl);
           else load_v_tile<T, 2>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
         });
         break;
       case 3:
         expand_chunks<T, TY, 3>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
-          if constexpr (kFused) load_v_parts<T, 3>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+          if constexpr (kFused) load_v_parts<T, 3>(pl, cb0, cb1, item.count, e.rank, Vh, Vl);
           else load_v_tile<T, 3>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
         });
         break;
       default:
         expand_chunks<T, TY, 4>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
-          if constexpr (kFused) load_v_parts<T, 4>(pl, j, lst, cb0, cb1, item.count, e.rank, Vh, Vl);
+          if constexpr (kFused) load_v_parts<T, 4>(pl, cb0, cb1, item.count, e.rank, Vh, Vl);
           else load_v_tile<T, 4>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
         });
         break;
     }
     lds_barrier();  // tokens and V are free (the y stores stay in flight)
-  }
+  });
 }
 
 }  // namespace lora

@@ -1,0 +1,118 @@
+// Block ranges and split-K contributions of the persistent MFMA kernels (see
+// layout.h).  The kernels walk the same ranges (kmfma.h, for_each_piece); a
+// CPU test replays that walk against this image.
+#include "layout.h"
+
+#include <algorithm>
+#include <climits>
+
+namespace lora {
+
+namespace {
+
+struct Pos {
+  int j, tile, k;
+};
+bool pos_lt(Pos a, Pos b) {
+  return a.j < b.j || (a.j == b.j && (a.tile < b.tile || (a.tile == b.tile && a.k < b.k)));
+}
+Pos pos_at(const int32_t* tab, int L) {
+  return Pos{tab[kPosInts * L], tab[kPosInts * L + 1], tab[kPosInts * L + 2]};
+}
+
+// The non-empty pieces (slice j, tile t, units [k0, k1)) of the range [a, b).
+template <class F>
+void for_pieces(Pos a, Pos b, int T, const std::vector<int32_t>& n, F&& f) {
+  Pos p = a;
+  while (pos_lt(p, b)) {
+    const int k1 = (p.j == b.j && p.tile == b.tile) ? b.k : n[(size_t)p.j];
+    f(p.j, p.tile, p.k, k1);
+    p.k = 0;
+    if (++p.tile == T) {
+      p.tile = 0;
+      ++p.j;
+    }
+  }
+}
+
+}  // namespace
+
+void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G,
+                    int32_t* out) {
+  const int T = (int)w.size(), J = (int)n.size();
+  int64_t per = 0, total = 0;
+  for (int32_t x : w) per += x;
+  for (int32_t nj : n) total += per * nj;
+  int j = 0, t = 0;
+  int64_t before = 0;  // weight of the units before tile t of slice j
+  for (int L = 0; L <= G; ++L) {
+    const int64_t target = total * L / G;
+    int32_t* o = out + kPosInts * L;
+    o[0] = J;
+    o[1] = o[2] = o[3] = 0;
+    while (j < J) {
+      const int64_t wt = w[(size_t)t];
+      const int64_t k = std::max<int64_t>(0, (target - before + wt - 1) / wt);
+      if (k < n[(size_t)j]) {
+        o[0] = j;
+        o[1] = t;
+        o[2] = (int32_t)k;
+        break;
+      }
+      before += wt * n[(size_t)j];
+      if (++t == T) {
+        t = 0;
+        ++j;
+      }
+    }
+  }
+}
+
+bool layout_host(const std::vector<int32_t>& ws, const std::vector<int32_t>& we,
+                 const std::vector<int32_t>& tu, const std::vector<int32_t>& nst,
+                 const std::vector<int32_t>& nch, int G, LayoutHost& h) {
+  const int J = (int)nst.size();
+  const int T = (int)ws.size();
+  h.o_bs = 0;
+  h.o_be = (size_t)kPosInts * ((size_t)G + 1);
+  h.o_fl = 2 * (size_t)kPosInts * ((size_t)G + 1);
+  h.o_off = (h.o_fl + 2 * (size_t)G + 3) & ~(size_t)3;
+  h.o_ent = (h.o_off + (size_t)J * ((size_t)T + 1) + 3) & ~(size_t)3;
+  std::vector<int32_t>& buf = h.buf;
+  buf.assign(h.o_ent, 0);
+  balance_ranges(ws, nst, G, buf.data() + h.o_bs);
+  balance_ranges(we, nch, G, buf.data() + h.o_be);
+  // per (j, tile) the blocks whose shrink ranges meet it, in block order; each
+  // block's first and last piece
+  std::vector<std::vector<int32_t>> lists((size_t)J * (size_t)T);
+  std::vector<Pos> first((size_t)G, Pos{-1, -1, 0}), last((size_t)G, Pos{-1, -1, 0});
+  for (int L = 0; L < G; ++L) {
+    const int32_t* bs = buf.data() + h.o_bs;
+    for_pieces(pos_at(bs, L), pos_at(bs, L + 1), T, nst, [&](int j, int t, int, int) {
+      lists[(size_t)j * T + t].push_back(L);
+      if (first[(size_t)L].j < 0) first[(size_t)L] = Pos{j, t, 0};
+      last[(size_t)L] = Pos{j, t, 0};
+    });
+  }
+  int64_t units = 0;
+  std::vector<int32_t> ent;
+  for (int j = 0; j < J; ++j) {
+    for (int t = 0; t < T; ++t) {
+      buf[h.o_off + (size_t)j * (T + 1) + t] = (int32_t)ent.size();
+      for (int32_t L : lists[(size_t)j * T + t]) {
+        if (units > INT32_MAX) return false;
+        if (first[(size_t)L].j == j && first[(size_t)L].tile == t) buf[h.o_fl + 2 * (size_t)L] = (int32_t)units;
+        if (last[(size_t)L].j == j && last[(size_t)L].tile == t) buf[h.o_fl + 2 * (size_t)L + 1] = (int32_t)units;
+        ent.push_back((int32_t)units);
+        units += tu[(size_t)t];
+      }
+    }
+    buf[h.o_off + (size_t)j * (T + 1) + T] = (int32_t)ent.size();
+  }
+  if (units > INT32_MAX) return false;
+  buf.insert(buf.end(), ent.begin(), ent.end());
+  h.part_units = units;
+  return true;
+}
+
+}  // namespace lora

@@ -1,0 +1,45 @@
+// Block ranges and split-K contributions of the persistent MFMA kernels for
+// one launch shape (host side, plain C++; no HIP dependency).
+//
+// A launch's work sequence is the MFMA tiles of launch slice 0, then those of
+// slice 1, ...; tile t of slice j has n[j] units (shrink stages or expand
+// chunks) of weight w[t] each.  The sequence is split into G contiguous ranges
+// of equal weight, one per block of the persistent grid.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+namespace lora {
+
+// A position {j, tile, k} in the sequence, as 4 int32 (the device RangePos).
+// Positions are normalized: k < n[j], tile < T, j < J, or the end {J, 0, 0}.
+constexpr int kPosInts = 4;
+
+// Block L's range is [pos[L], pos[L + 1]): pos[L] is the first unit whose
+// cumulative start weight is at least total * L / G.  out: (G + 1) positions.
+void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G,
+                    int32_t* out);
+
+// The int32 image of a launch shape's layout, copied to the device as is:
+//   [o_bs]  shrink ranges, (G + 1) positions (stage units, weights ws)
+//   [o_be]  expand ranges, (G + 1) positions (chunk units, weights we)
+//   [o_fl]  per block: float4 offsets of the partial tiles of the first and
+//           the last piece of its shrink range (a piece between them covers a
+//           whole tile, the tile's only contribution)
+//   [o_off] per (j, tile): first contribution index, J * (T + 1) entries
+//   [o_ent] contributions in (j, tile, block) order: float4 offset of each
+//           partial tile (tile t's partials hold tu[t] float4 units)
+struct LayoutHost {
+  std::vector<int32_t> buf;
+  size_t o_bs = 0, o_be = 0, o_fl = 0, o_off = 0, o_ent = 0;
+  int64_t part_units = 0;  // float4 units of all partial tiles
+};
+
+// False if the partial tiles would exceed 2^31 float4 units.
+bool layout_host(const std::vector<int32_t>& ws, const std::vector<int32_t>& we,
+                 const std::vector<int32_t>& tu, const std::vector<int32_t>& nst,
+                 const std::vector<int32_t>& nch, int G, LayoutHost& h);
+
+}  // namespace lora

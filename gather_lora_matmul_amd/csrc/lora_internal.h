@@ -66,7 +66,6 @@ struct PlanItem {
 
 constexpr int kShortG = 4;   // tokens per short item
 constexpr int kTileM = 64;   // tokens per MFMA tile
-constexpr int kVgLd = LORA_MAX_RANK;  // floats per slot of a partial tile
 constexpr int kMaxNpa = 8;            // MFMA tiles: pages per A row, at most
 
 // ---- kernel launchers (defined in the .hip files) -------------------------
@@ -86,38 +85,39 @@ hipError_t launch_bgmv_expand(int dtype, int y_dtype, const PoolView& pv, const 
 hipError_t launch_bgmv_apply(int dtype, int y_dtype, const PoolView& pv, const IoSet& ios,
                              const int32_t* ids, int32_t n, hipStream_t s);
 
-// Start of one block's share of the MFMA tiles (persistent kernels): the tile
-// holding the block's first unit of work and the offset into that tile in
-// weight units (w = the tile's weight per stage or chunk).  In a slice whose
-// tiles have n stages (or chunks), the block starts at stage ceil(n*off/w) of
-// `tile`; consecutive entries delimit a block's range.
-struct BlockStart {
+// Position in a launch's sequence of MFMA work for the persistent kernels:
+// the tiles of launch slice 0, then those of slice 1, ...; unit k of a tile is
+// a shrink stage (64 columns of d_in) or an expand chunk (64 rows of d_out).
+// A position is normalized (k < units of the tile, tile < n_mfma, j < n_io) or
+// is the end {n_io, 0, 0}; block L's range is [pos[L], pos[L + 1]).
+struct RangePos {
+  int32_t j;
   int32_t tile;
-  int32_t off;
-  int32_t w;
+  int32_t k;
   int32_t pad;
 };
 
-// Items [0, n_mfma) are MFMA tiles, [n_mfma, n_items) short items.
+// Items [0, n_mfma) are MFMA tiles, [n_mfma, n_items) short items.  The range
+// tables and the split-K contributions belong to one launch shape (the stage
+// and chunk counts of the launch's slices); a plan keeps a few such layouts.
 struct PlanView {
   const PlanItem* items;
   const int32_t* perm;
-  const BlockStart* bs_shrink;   // [G + 1]
-  const BlockStart* bs_expand;   // [G + 1]
-  // split-K contributors of each MFMA tile's shrink, per pool slice s: the
-  // entries [contrib_off[s][i], contrib_off[s][i + 1]) of contrib[s] list the
-  // blocks whose shrink ranges meet tile i, in block order, as pairs
-  // {(L << 1) | side, float4 offset of the contribution's partial tile}
-  const int32_t* contrib_off;    // [n_slices][tile_cap + 1]
-  const int32_t* contrib;        // [n_slices][contrib_cap][2]
-  float* part;                   // partial tiles [n_io][part_stride] float4
+  const RangePos* bs_shrink;   // [G + 1]
+  const RangePos* bs_expand;   // [G + 1]
+  // Split-K shrink: float4 offsets (into part) of block L's partial tiles for
+  // the first and the last piece of its range.  A piece between them covers a
+  // whole tile, whose only contribution is c_ent[c_off[j][tile]].
+  const int2* part_fl;         // [G]
+  // contributions to tile i of launch slice j, in block order: the partial
+  // tiles at float4 offsets c_ent[c_off[j][i] .. c_off[j][i + 1])
+  const int32_t* c_off;        // [n_io][n_mfma + 1]
+  const int32_t* c_ent;
+  float* part;                 // partial tiles
   int32_t n_items;
   int32_t n_tokens;
   int32_t n_mfma;
-  int32_t G;                     // persistent grid (blocks)
-  int32_t tile_cap;              // max tiles = max tokens
-  int32_t contrib_cap;           // entries of contrib per slice
-  int64_t part_stride;           // float4 units of partial tiles per launch slice
+  int32_t G;                   // persistent grid (blocks)
 };
 
 hipError_t launch_sgmv_shrink(int dtype, const PoolView& pv, const PlanView& pl,

@@ -13,107 +13,97 @@
 #include <algorithm>
 #include <cstring>
 
+#include "layout.h"
 #include "runtime.h"
 
 using namespace lora;
 
-namespace {
-
-// Split the weighted tile list w[0..n) into G contiguous ranges of equal
-// weight (persistent kernels: logical block L takes [out[L], out[L+1])).
-// Range boundaries fall inside tiles; a kernel rounds them to the stage or
-// chunk grid of the slice it runs.
-void balance_blocks(const std::vector<int32_t>& w, int G, BlockStart* out) {
-  const int n = (int)w.size();
-  int64_t total = 0;
-  for (int32_t x : w) total += x;
-  int i = 0;
-  int64_t before = 0;  // weight of tiles [0, i)
-  for (int L = 0; L <= G; ++L) {
-    const int64_t pos = total * L / G;
-    while (i < n && before + w[(size_t)i] <= pos) before += w[(size_t)i++];
-    if (i >= n) {
-      out[L] = BlockStart{n, 0, 1, 0};
-    } else {
-      out[L] = BlockStart{i, (int32_t)(pos - before), w[(size_t)i], 0};
-    }
-  }
-}
-
-// First unit of logical block L in a slice whose tiles have n units: the
-// kernels' rounding of the BlockStart table, replicated exactly.
-struct HPos {
-  int tile, k;
-};
-HPos range_start_host(const BlockStart* bs, int L, int n, int n_tiles) {
-  const BlockStart b = bs[L];
-  if (b.tile >= n_tiles) return HPos{n_tiles, 0};
-  const int k = (int)(((uint32_t)n * (uint32_t)b.off + (uint32_t)b.w - 1u) / (uint32_t)b.w);
-  if (k >= n) return HPos{b.tile + 1, 0};
-  return HPos{b.tile, k};
-}
-bool hpos_lt(HPos a, HPos b) { return a.tile < b.tile || (a.tile == b.tile && a.k < b.k); }
-
-// Contributor lists of the split-K shrink for every pool slice (its d_in fixes
-// the stage count): per tile, the blocks whose ranges meet it, in block order,
-// as {(L << 1) | side, offset of the contribution's partial tile} (side 0: the
-// tile is the first of the block's range).  A partial tile holds
-// ceil(rank / 16) * ceil(count / 16) * 64 float4 units; the offsets of a slice
-// run from 0 to at most part_stride.
-void shrink_contributors(lora_plan* pl, int n_tiles, const std::vector<int32_t>& tile_units) {
-  const lora_pool* p = pl->pool;
-  const int G = pl->G;
-  const size_t offn = (size_t)pl->max_tokens + 1;
-  pl->h_contrib.assign((size_t)p->n_slices * (offn + 2 * (size_t)pl->contrib_cap), 0);
-  pl->part_stride = 0;
-  std::vector<std::vector<int32_t>> lists((size_t)n_tiles);
-  for (int s = 0; s < p->n_slices; ++s) {
-    const int nst = (p->d_in[(size_t)s] + 63) / 64;
-    for (auto& l : lists) l.clear();
-    HPos a = range_start_host(pl->h_bs.data(), 0, nst, n_tiles);
-    for (int L = 0; L < G; ++L) {
-      const HPos b = range_start_host(pl->h_bs.data(), L + 1, nst, n_tiles);
-      for (int i = a.tile; i < n_tiles && hpos_lt(HPos{i, 0}, b); ++i) {
-        const int k0 = i == a.tile ? a.k : 0;
-        const int k1 = i == b.tile ? b.k : nst;
-        if (k0 < k1) lists[(size_t)i].push_back((L << 1) | (i == a.tile ? 0 : 1));
-      }
-      a = b;
-    }
-    int32_t* off = pl->h_contrib.data() + (size_t)s * offn;
-    int32_t* ent = pl->h_contrib.data() + (size_t)p->n_slices * offn + (size_t)s * 2 * pl->contrib_cap;
-    int32_t pos = 0;
-    int64_t units = 0;
-    for (int i = 0; i < n_tiles; ++i) {
-      off[i] = pos;
-      for (int32_t x : lists[(size_t)i]) {
-        ent[2 * pos] = x;
-        ent[2 * pos + 1] = (int32_t)units;
-        units += tile_units[(size_t)i];
-        ++pos;
-      }
-    }
-    off[n_tiles] = pos;
-    pl->part_stride = std::max(pl->part_stride, units);
-  }
-}
-
-}  // namespace
+static_assert(sizeof(RangePos) == kPosInts * sizeof(int32_t), "device positions are 4 int32");
 
 namespace lora {
-lora_status plan_reserve_part(lora_plan* pl, int n_io) {
-  const size_t need = (size_t)n_io * (size_t)pl->part_stride * 4;  // floats
-  if (need <= pl->part_cap) return LORA_OK;
-  if (pl->d_part) {
-    LORA_HIP(hipDeviceSynchronize());  // earlier launches may still use the old buffer
-    (void)hipFree(pl->d_part);
-    pl->d_part = nullptr;
-    pl->part_cap = 0;
+
+lora_status plan_layout(lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out) {
+  const int J = ios.n_io;
+  const int T = pl->n_mfma;
+  const int G = pl->G;
+  std::vector<int32_t> nst((size_t)J), nch((size_t)J);
+  std::vector<int32_t> key;
+  key.push_back(J);
+  for (int j = 0; j < J; ++j) {
+    nst[(size_t)j] = (ios.io[j].d_in + 63) / 64;
+    nch[(size_t)j] = (ios.io[j].d_out + 63) / 64;
+    key.push_back(nst[(size_t)j]);
+    key.push_back(nch[(size_t)j]);
   }
-  LORA_HIP(hipMalloc((void**)&pl->d_part, sizeof(float) * need));
-  pl->part_cap = need;
+  PlanLayout* lay = nullptr;
+  for (PlanLayout& l : pl->layouts)
+    if (l.valid && l.key == key) lay = &l;
+  if (!lay) {
+    // build: the least recently used slot
+    lay = &pl->layouts[0];
+    for (PlanLayout& l : pl->layouts)
+      if (!l.valid || l.used < lay->used) lay = &l;
+    lay->valid = false;
+    LayoutHost h;
+    if (!layout_host(pl->h_ws, pl->h_we, pl->h_tu, nst, nch, G, h))
+      return fail(LORA_E_ARG, "plan: partial-tile workspace exceeds 2^31 float4 units");
+    const std::vector<int32_t>& buf = h.buf;
+    const int64_t units = h.part_units;
+    const size_t bytes = sizeof(int32_t) * buf.size();
+    if (lay->ev_pending) {  // the staging buffer of this slot may still be copied from
+      LORA_HIP(hipEventSynchronize(lay->ev));
+      lay->ev_pending = false;
+    }
+    if (bytes > lay->cap) {
+      if (lay->d_buf) {
+        LORA_HIP(hipDeviceSynchronize());  // earlier launches may still read it
+        (void)hipFree(lay->d_buf);
+        lay->d_buf = nullptr;
+      }
+      if (lay->h_buf) (void)hipHostFree(lay->h_buf);
+      lay->h_buf = nullptr;
+      lay->cap = 0;
+      const size_t cap = bytes + bytes / 2 + 4096;
+      LORA_HIP(hipMalloc((void**)&lay->d_buf, cap));
+      hipError_t e = hipHostMalloc((void**)&lay->h_buf, cap, hipHostMallocDefault);
+      if (e != hipSuccess) {
+        (void)hipFree(lay->d_buf);
+        lay->d_buf = nullptr;
+        return fail(LORA_E_HIP, "plan layout staging: %s", hipGetErrorString(e));
+      }
+      lay->cap = cap;
+    }
+    if (!lay->ev) LORA_HIP(hipEventCreateWithFlags(&lay->ev, hipEventDisableTiming));
+    memcpy(lay->h_buf, buf.data(), bytes);
+    LORA_HIP(hipMemcpyAsync(lay->d_buf, lay->h_buf, bytes, hipMemcpyHostToDevice, s));
+    LORA_HIP(hipEventRecord(lay->ev, s));
+    lay->ev_pending = true;
+    lay->key = key;
+    lay->part_units = units;
+    lay->o_bs = h.o_bs;
+    lay->o_be = h.o_be;
+    lay->o_fl = h.o_fl;
+    lay->o_off = h.o_off;
+    lay->o_ent = h.o_ent;
+    lay->valid = true;
+  }
+  lay->used = ++pl->layout_clock;
+  // partial-tile workspace
+  const size_t need = 4 * (size_t)lay->part_units;  // floats
+  if (need > pl->part_cap) {
+    if (pl->d_part) {
+      LORA_HIP(hipDeviceSynchronize());  // earlier launches may still use the old buffer
+      (void)hipFree(pl->d_part);
+      pl->d_part = nullptr;
+      pl->part_cap = 0;
+    }
+    LORA_HIP(hipMalloc((void**)&pl->d_part, sizeof(float) * need));
+    pl->part_cap = need;
+  }
+  *out = lay;
   return LORA_OK;
 }
+
 }  // namespace lora
 
 extern "C" {
@@ -138,17 +128,10 @@ lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** ou
     }
     pl->G = ((2 * ncu + 7) / 8) * 8;
     const size_t tok = (size_t)max_tokens;
-    pl->contrib_cap = 2 * pl->G + max_tokens + 8;
-    const size_t ncontrib = (size_t)pool->n_slices * ((size_t)max_tokens + 1 + 2 * (size_t)pl->contrib_cap);
-    const size_t need = sizeof(int32_t) * tok + sizeof(PlanItem) * tok + 256 +
-                        sizeof(BlockStart) * 2 * ((size_t)pl->G + 1) + 256 + sizeof(int32_t) * ncontrib + 256;
+    const size_t need = sizeof(int32_t) * tok + sizeof(PlanItem) * tok + 256;
     e = hipHostMalloc((void**)&pl->h_pinned, need, hipHostMallocDefault);
     if (e == hipSuccess) e = hipMalloc((void**)&pl->d_perm, sizeof(int32_t) * tok);
     if (e == hipSuccess) e = hipMalloc((void**)&pl->d_items, sizeof(PlanItem) * tok);
-    if (e == hipSuccess) e = hipMalloc((void**)&pl->d_bs, sizeof(BlockStart) * 2 * ((size_t)pl->G + 1));
-    if (pool->dtype != LORA_F32) {  // MFMA tiles exist only on 16-bit pools
-      if (e == hipSuccess) e = hipMalloc((void**)&pl->d_contrib, sizeof(int32_t) * ncontrib);
-    }
     if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->ev, hipEventDisableTiming);
     if (e != hipSuccess) {
       lora_plan_destroy(pl);
@@ -167,13 +150,20 @@ lora_status lora_plan_destroy(lora_plan* pl) {
     (void)hipEventSynchronize(pl->ev);
     (void)hipEventDestroy(pl->ev);
   }
+  for (PlanLayout& l : pl->layouts)
+    if (l.ev) {
+      (void)hipEventSynchronize(l.ev);
+      (void)hipEventDestroy(l.ev);
+    }
   if (pl->h_pinned) (void)hipHostFree(pl->h_pinned);
   if (pl->d_perm || pl->d_part) (void)hipDeviceSynchronize();  // launches may still read them
   if (pl->d_perm) (void)hipFree(pl->d_perm);
   if (pl->d_items) (void)hipFree(pl->d_items);
-  if (pl->d_bs) (void)hipFree(pl->d_bs);
   if (pl->d_part) (void)hipFree(pl->d_part);
-  if (pl->d_contrib) (void)hipFree(pl->d_contrib);
+  for (PlanLayout& l : pl->layouts) {
+    if (l.d_buf) (void)hipFree(l.d_buf);
+    if (l.h_buf) (void)hipHostFree(l.h_buf);
+  }
   delete pl;
   return LORA_OK;
 }
@@ -255,12 +245,18 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
   });
   pl->h_items.clear();
   for (const Keyed& k : items) pl->h_items.push_back(k.it);
-  if (pl->G > 0) {
+  {
     // Weights of the MFMA tiles (items [0, n_mfma)) per shrink stage and per
-    // expand chunk, in 128-byte rows moved: x rows (16 per token block) plus A
-    // rows for a shrink stage; y rows read and written plus B rows for an
-    // expand chunk; +16 for the fixed per-step cost.
-    std::vector<int32_t> ws((size_t)n_mfma), we((size_t)n_mfma), tu((size_t)n_mfma);
+    // expand chunk, in 128-byte rows moved, and the size of a partial tile.
+    // The range tables and contributions are built per launch shape
+    // (plan_layout); the plan's old ones are dropped here.
+    std::vector<int32_t>& ws = pl->h_ws;
+    std::vector<int32_t>& we = pl->h_we;
+    std::vector<int32_t>& tu = pl->h_tu;
+    ws.assign((size_t)n_mfma, 0);
+    we.assign((size_t)n_mfma, 0);
+    tu.assign((size_t)n_mfma, 0);
+    for (PlanLayout& l : pl->layouts) l.valid = false;
     for (int i = 0; i < n_mfma; ++i) {
       const PlanItem& it = pl->h_items[(size_t)i];
       int rmax = 0;
@@ -273,10 +269,6 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
       we[(size_t)i] = 256 + 2 * it.count + p->rs_of(rmax) / 2;
       tu[(size_t)i] = (rp / 16) * ((it.count + 15) / 16) * 64;
     }
-    pl->h_bs.assign(2 * ((size_t)pl->G + 1), BlockStart{0, 0, 1, 0});
-    balance_blocks(ws, pl->G, pl->h_bs.data());
-    balance_blocks(we, pl->G, pl->h_bs.data() + pl->G + 1);
-    if (pl->d_contrib) shrink_contributors(pl, n_mfma, tu);
   }
   pl->n_tokens = n;
   pl->n_groups = groups;
@@ -291,20 +283,10 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
     const size_t pb = sizeof(int32_t) * (size_t)n;
     const size_t ioff = (pb + 255) & ~(size_t)255;
     const size_t ib = sizeof(PlanItem) * pl->h_items.size();
-    const size_t boff = (ioff + ib + 255) & ~(size_t)255;
-    const size_t bb = sizeof(BlockStart) * pl->h_bs.size();
     memcpy(pl->h_pinned, pl->h_perm.data(), pb);
     memcpy(pl->h_pinned + ioff, pl->h_items.data(), ib);
-    memcpy(pl->h_pinned + boff, pl->h_bs.data(), bb);
     LORA_HIP(hipMemcpyAsync(pl->d_perm, pl->h_pinned, pb, hipMemcpyHostToDevice, s));
     LORA_HIP(hipMemcpyAsync(pl->d_items, pl->h_pinned + ioff, ib, hipMemcpyHostToDevice, s));
-    LORA_HIP(hipMemcpyAsync(pl->d_bs, pl->h_pinned + boff, bb, hipMemcpyHostToDevice, s));
-    if (pl->d_contrib && n_mfma > 0) {
-      const size_t coff = (boff + bb + 255) & ~(size_t)255;
-      const size_t cb = sizeof(int32_t) * pl->h_contrib.size();
-      memcpy(pl->h_pinned + coff, pl->h_contrib.data(), cb);
-      LORA_HIP(hipMemcpyAsync(pl->d_contrib, pl->h_pinned + coff, cb, hipMemcpyHostToDevice, s));
-    }
     LORA_HIP(hipEventRecord(pl->ev, s));
     pl->ev_pending = true;
   }

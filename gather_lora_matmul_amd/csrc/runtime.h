@@ -97,9 +97,27 @@ struct lora_pool {
 
 struct lora_plan;
 namespace lora {
-// Grow the plan's split-K partial workspace to hold n_io slices (allocation
-// happens at most once per size increase; the first launches pay for it).
-lora_status plan_reserve_part(lora_plan* pl, int n_io);
+// The range tables and split-K contributions of one launch shape (n_io, then
+// the stage and chunk counts of each launch slice), built on the host at the
+// first launch of that shape after a plan build and copied to the device on
+// the launch stream.
+struct PlanLayout {
+  std::vector<int32_t> key;
+  bool valid = false;
+  uint64_t used = 0;          // LRU clock
+  int32_t* d_buf = nullptr;   // device copy: ranges, part_fl, c_off, c_ent
+  char* h_buf = nullptr;      // pinned staging of the same
+  size_t cap = 0;             // bytes of each
+  hipEvent_t ev = nullptr;    // the staging copy has been consumed
+  bool ev_pending = false;
+  int64_t part_units = 0;     // float4 units of partial tiles
+  size_t o_bs = 0, o_be = 0, o_fl = 0, o_off = 0, o_ent = 0;  // int32 offsets
+};
+constexpr int kPlanLayouts = 4;
+
+// Layout for the launch slices of `ios` (built and uploaded on `s` if the plan
+// has none of that shape), with the plan's partial-tile workspace grown to it.
+lora_status plan_layout(lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out);
 }  // namespace lora
 
 struct lora_plan {
@@ -121,32 +139,29 @@ struct lora_plan {
   bool ev_pending = false;
   int32_t* d_perm = nullptr;
   lora::PlanItem* d_items = nullptr;
-  // persistent MFMA kernels: grid, block-range tables and device work buffers
+  // persistent MFMA kernels: grid, per-tile weights and launch-shape layouts
   int32_t G = 0;
-  std::vector<lora::BlockStart> h_bs;       // [2][G + 1]: shrink, expand
-  lora::BlockStart* d_bs = nullptr;
-  int32_t contrib_cap = 0;                  // per slice: 2 G + max_tokens + 8
-  int64_t part_stride = 0;                  // float4 units of partial tiles per launch slice
-  std::vector<int32_t> h_contrib;           // [n_slices][max_tokens + 1] offsets, then [n_slices][contrib_cap][2]
-  int32_t* d_contrib = nullptr;
-  float* d_part = nullptr;                  // grown on demand: [n_io][part_stride] float4
-  size_t part_cap = 0;                      // floats
-  lora::PlanView view() const {
+  std::vector<int32_t> h_ws;  // per MFMA tile: weight of one shrink stage
+  std::vector<int32_t> h_we;  //   ... of one expand chunk
+  std::vector<int32_t> h_tu;  //   ... float4 units of one partial tile
+  lora::PlanLayout layouts[lora::kPlanLayouts];
+  uint64_t layout_clock = 0;
+  float* d_part = nullptr;    // partial tiles, grown on demand
+  size_t part_cap = 0;        // floats
+  lora::PlanView view(const lora::PlanLayout* lay) const {
     lora::PlanView v;
     v.items = d_items;
     v.perm = d_perm;
-    v.bs_shrink = d_bs;
-    v.bs_expand = d_bs ? d_bs + (G + 1) : nullptr;
-    v.contrib_off = d_contrib;
-    v.contrib = d_contrib ? d_contrib + (size_t)pool->n_slices * (max_tokens + 1) : nullptr;
-    v.contrib_cap = contrib_cap;
-    v.part_stride = part_stride;
+    v.bs_shrink = lay ? reinterpret_cast<const lora::RangePos*>(lay->d_buf + lay->o_bs) : nullptr;
+    v.bs_expand = lay ? reinterpret_cast<const lora::RangePos*>(lay->d_buf + lay->o_be) : nullptr;
+    v.part_fl = lay ? reinterpret_cast<const int2*>(lay->d_buf + lay->o_fl) : nullptr;
+    v.c_off = lay ? lay->d_buf + lay->o_off : nullptr;
+    v.c_ent = lay ? lay->d_buf + lay->o_ent : nullptr;
     v.part = d_part;
     v.n_items = n_items;
     v.n_tokens = n_tokens;
     v.n_mfma = n_mfma;
     v.G = G;
-    v.tile_cap = max_tokens;
     return v;
   }
 };

@@ -1,0 +1,128 @@
+// Host check of the persistent MFMA kernels' block ranges (layout.cpp): on
+// seeded random launch shapes, every unit of the work sequence belongs to
+// exactly one block, positions are normalized and monotone, the weight of a
+// block's range is within one unit of the mean, and replaying the kernels'
+// walk (first / last piece flags, as for_each_piece in kmfma.h computes them)
+// finds each piece's partial tile at the offset listed for that block in the
+// tile's contributions, in block order, with disjoint offsets.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+
+#include "layout.h"
+
+using lora::LayoutHost;
+using lora::kPosInts;
+
+namespace {
+struct P {
+  int j, t, k;
+};
+bool lt(P a, P b) { return a.j < b.j || (a.j == b.j && (a.t < b.t || (a.t == b.t && a.k < b.k))); }
+P at(const int32_t* tab, int L) { return P{tab[kPosInts * L], tab[kPosInts * L + 1], tab[kPosInts * L + 2]}; }
+}  // namespace
+
+int main(int argc, char** argv) {
+  const int trials = argc > 1 ? atoi(argv[1]) : 2000;
+  std::mt19937 rng(20261203);
+  int bad = 0;
+  auto fail = [&](const char* what, int trial) {
+    if (bad++ < 10) printf("FAIL trial %d: %s\n", trial, what);
+  };
+  for (int trial = 0; trial < trials; ++trial) {
+    const int T = 1 + rng() % 300, J = 1 + rng() % 8, G = 8 * (1 + rng() % 64);
+    std::vector<int32_t> ws(T), we(T), tu(T), nst(J), nch(J);
+    for (int t = 0; t < T; ++t) {
+      ws[t] = 1 + rng() % ((trial % 3 == 0) ? 1000 : 50);
+      we[t] = 1 + rng() % 300;
+      tu[t] = 64 * (1 + rng() % 32);
+    }
+    for (int j = 0; j < J; ++j) {
+      nst[j] = 1 + rng() % ((trial % 5 == 0) ? 3 : 400);
+      nch[j] = 1 + rng() % 400;
+    }
+    LayoutHost h;
+    if (!lora::layout_host(ws, we, tu, nst, nch, G, h)) {
+      fail("layout_host refused", trial);
+      continue;
+    }
+    const int32_t* fl = h.buf.data() + h.o_fl;
+    const int32_t* coff = h.buf.data() + h.o_off;
+    const int32_t* cent = h.buf.data() + h.o_ent;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int32_t* tab = h.buf.data() + (pass ? h.o_be : h.o_bs);
+      const std::vector<int32_t>& n = pass ? nch : nst;
+      const std::vector<int32_t>& w = pass ? we : ws;
+      std::vector<std::vector<int>> cover((size_t)J * T);
+      for (int j = 0; j < J; ++j)
+        for (int t = 0; t < T; ++t) cover[(size_t)j * T + t].assign(n[j], 0);
+      const P a0 = at(tab, 0), aG = at(tab, G);
+      if (!(a0.j == 0 && a0.t == 0 && a0.k == 0) || !(aG.j == J && aG.t == 0 && aG.k == 0)) fail("ends", trial);
+      double total = 0, wmax = 0;
+      for (int j = 0; j < J; ++j)
+        for (int t = 0; t < T; ++t) total += (double)n[j] * w[t];
+      for (int x : w) wmax = std::max(wmax, (double)x);
+      for (int L = 0; L < G; ++L) {
+        const P a = at(tab, L), b = at(tab, L + 1);
+        if (lt(b, a)) fail("not monotone", trial);
+        if (b.j < J && !(b.t < T && b.k < n[b.j])) fail("not normalized", trial);
+        // the kernels' walk
+        int j = a.j, t = a.t, k = a.k;
+        bool first = true;
+        double wsum = 0;
+        while (lt(P{j, t, k}, b)) {
+          const bool ends_here = j == b.j && t == b.t;
+          const int k1 = ends_here ? b.k : n[j];
+          int nj = j, nt = t + 1;
+          if (nt == T) {
+            nt = 0;
+            ++nj;
+          }
+          const bool last = ends_here || !lt(P{nj, nt, 0}, b);
+          if (!(k < k1)) fail("empty piece", trial);
+          for (int kk = k; kk < k1; ++kk) cover[(size_t)j * T + t][kk]++;
+          wsum += (double)(k1 - k) * w[t];
+          if (pass == 0) {
+            const int32_t off = first ? fl[2 * L] : last ? fl[2 * L + 1] : cent[coff[j * (T + 1) + t]];
+            // block L's index among the tile's contributors (blocks whose
+            // non-empty ranges meet the tile), in block order
+            int idx = 0, found = -1;
+            for (int M = 0; M < G; ++M) {
+              const P c = at(tab, M), d = at(tab, M + 1);
+              if (lt(c, d) && lt(c, P{j, t, n[j]}) && lt(P{j, t, 0}, d)) {
+                if (M == L) found = idx;
+                ++idx;
+              }
+            }
+            const int c0 = coff[j * (T + 1) + t], c1 = coff[j * (T + 1) + t + 1];
+            if (found < 0 || c1 - c0 != idx || cent[c0 + found] != off) fail("contribution offset", trial);
+            if (!first && !last && c1 - c0 != 1) fail("middle piece shared", trial);
+          }
+          first = false;
+          j = nj;
+          t = nt;
+          k = 0;
+        }
+        if (wsum > total / G + wmax + 1e-6) fail("imbalance", trial);
+      }
+      for (auto& c : cover)
+        for (int x : c)
+          if (x != 1) {
+            fail("unit not covered exactly once", trial);
+            break;
+          }
+    }
+    int64_t expect = 0;
+    for (int j = 0; j < J; ++j)
+      for (int t = 0; t < T; ++t)
+        for (int c = coff[j * (T + 1) + t]; c < coff[j * (T + 1) + t + 1]; ++c) {
+          if (cent[c] != expect) fail("partial offsets not disjoint", trial);
+          expect += tu[t];
+        }
+    if (expect != h.part_units || (size_t)coff[J * (T + 1) - 1] != h.buf.size() - h.o_ent)
+      fail("partial units", trial);
+  }
+  printf("%d trials, %d failures\n", trials, bad);
+  return bad != 0;
+}
