@@ -3,6 +3,7 @@
 // y_i += s_a B_a (A_a x_i) with a different adapter -- and possibly a different
 // rank -- per token, every adapter row gathered through the page table of the
 // unified pool (section "Unified Paging").
+#include <algorithm>
 #include <cstdlib>
 
 #include "kvalu.h"
@@ -207,8 +208,10 @@ __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
   int unit, q;
   xcd_unit_split(blockIdx.x, nsplit, unit, q);
   if (unit >= n * ios.n_io) return;
-  const int i = unit / ios.n_io;
-  const int io_i = unit - i * ios.n_io;
+  // slice-major: the launcher puts the costliest slices first, so their units
+  // are dispatched first and the cheaper ones fill the compute units that free up
+  const int io_i = unit / n;
+  const int i = unit - io_i * n;
   const IoDesc io = ios.io[io_i];
   const int a = ids[i];
   if (a < 0) return;
@@ -307,9 +310,15 @@ inline int env_int(const char* name) {
 }
 
 template <typename T, typename TY>
-hipError_t apply_t(const PoolView& pv, const IoSet& ios, const int32_t* ids, int n,
+hipError_t apply_t(const PoolView& pv, const IoSet& ios_in, const int32_t* ids, int n,
                    hipStream_t s) {
   constexpr int E = ET<T>::E;
+  // slices by decreasing bytes per token unit (d_in + d_out): blocks are
+  // dispatched in unit order, so the longest units start first
+  IoSet ios = ios_in;
+  std::stable_sort(ios.io, ios.io + ios.n_io, [](const IoDesc& a, const IoDesc& b) {
+    return a.d_in + a.d_out > b.d_in + b.d_out;
+  });
   const int units = n * ios.n_io;
   static const int force_split = env_int("LORA_BGMV_SPLIT");
   static const int force_nt = env_int("LORA_BGMV_NT");
