@@ -75,6 +75,7 @@ template <typename T, typename TY, int NT, int U, int NCH>
 __device__ __forceinline__ void bgmv_fused_body(const PoolView& pv, const DevEntry& e,
                                                 const IoDesc& io, int i, int m_lo, int m_hi,
                                                 float* part, float* vsh) {
+  constexpr int kKB = U == 1 ? 16 : 8;  // A rows per batch (16-byte loads per thread: kKB * U)
   const char* xr[1] = {reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * sizeof(T)};
   char* yrow = reinterpret_cast<char*>(io.y) + (int64_t)i * io.d_out * sizeof(TY);
   const float s = e.scale;
@@ -82,13 +83,13 @@ __device__ __forceinline__ void bgmv_fused_body(const PoolView& pv, const DevEnt
     ExpandPrefetch<T, TY, NT, NCH> pf;
     const int m0 = m_lo + (int)threadIdx.x;
     pf.load(pv, e, yrow, m0, m_hi);
-    valu_shrink<T, NT, U, 1, 16>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
+    valu_shrink<T, NT, U, 1, kKB>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
     pf.finish(vsh, s, yrow, m0, m_hi);
     char* yr[1] = {yrow};
     valu_expand<T, TY, NT, NCH, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo + NT * ExpandPrefetch<T, TY, NT, NCH>::RU,
                                    m_hi);
   } else {
-    valu_shrink<T, NT, U, 1, 16>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
+    valu_shrink<T, NT, U, 1, kKB>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
     char* yr[1] = {yrow};
     valu_expand<T, TY, NT, 0, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo, m_hi);
   }

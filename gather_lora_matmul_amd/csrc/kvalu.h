@@ -243,22 +243,34 @@ __device__ __forceinline__ void valu_expand_any(const PoolView& pv, const DevEnt
                                                 char* const* yrow, int m_lo, int m_hi) {
   constexpr int E = ET<T>::E;
   // multi-token items keep the unrolled bodies small (v of G tokens per chunk)
+  // and instantiate only the short-row bodies they use
   const int nch = e.rs / E;
-  switch (G > 1 && nch > 4 ? 0 : nch) {
 #define LORA_NCH_CASE(N) \
   case N:                \
     valu_expand<T, TY, NT, N, G>(pv, e, vsh, VS, sg, yrow, m_lo, m_hi); \
     break;
-    LORA_NCH_CASE(1)
-    LORA_NCH_CASE(2)
-    LORA_NCH_CASE(3)
-    LORA_NCH_CASE(4)
-    LORA_NCH_CASE(6)
-    LORA_NCH_CASE(8)
-#undef LORA_NCH_CASE
-    default:
-      valu_expand<T, TY, NT, 0, G>(pv, e, vsh, VS, sg, yrow, m_lo, m_hi);
+  if constexpr (G > 1) {
+    switch (nch) {
+      LORA_NCH_CASE(1)
+      LORA_NCH_CASE(2)
+      LORA_NCH_CASE(3)
+      LORA_NCH_CASE(4)
+      default:
+        valu_expand<T, TY, NT, 0, G>(pv, e, vsh, VS, sg, yrow, m_lo, m_hi);
+    }
+  } else {
+    switch (nch) {
+      LORA_NCH_CASE(1)
+      LORA_NCH_CASE(2)
+      LORA_NCH_CASE(3)
+      LORA_NCH_CASE(4)
+      LORA_NCH_CASE(6)
+      LORA_NCH_CASE(8)
+      default:
+        valu_expand<T, TY, NT, 0, G>(pv, e, vsh, VS, sg, yrow, m_lo, m_hi);
+    }
   }
+#undef LORA_NCH_CASE
 }
 
 }  // namespace lora
