@@ -114,6 +114,9 @@ def main():
                              "llama70b_mixed_apply"])
     ap.add_argument("--batches", type=int, default=None,
                     help="rotating batches (default 16 for decode, 4 for planned batches)")
+    ap.add_argument("--l-long", type=int, default=0,
+                    help="planned batches: groups shorter than this run as short VALU items "
+                         "(0: every group of a 16-bit pool is an MFMA tile)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 64 MiB device copy 10x (HBM counter calibration)")
@@ -150,7 +153,7 @@ def main():
     if planned:
         for b in batches:
             p = L.lora_plan_create(sp.handle, len(b.ids))
-            L.lora_plan_build(p, b.ids)
+            L.lora_plan_build(p, b.ids, args.l_long)
             plans.append(p)
     stream = torch.cuda.current_stream()
 

@@ -607,6 +607,128 @@ __device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry
   }
 }
 
+// Tiles of at most 16 tokens (one token block; decode groups): steps of JB
+// chunks (64 JB output rows), wave w computing rows [16 JB w, 16 JB (w + 1))
+// of the step as JB 16-row MFMA blocks (JB = 4 up to rank 64, 2 above).  A
+// step moves JB chunks' B rows while y (<= 16 tokens) stays small, so each
+// round trip carries JB times the bytes of a 64-row chunk; B and y of the next
+// step are in flight while a step is computed.  Rows past the range's last
+// chunk (or d_out) are not written.
+template <typename T, typename TY, int NK, typename LoadV>
+__device__ __forceinline__ void expand_chunks_wide(const PoolView& pv, const DevEntry& e,
+                                                   const IoDesc& io, const int* toks, int count,
+                                                   int c0, int c1, const uint16_t* Vh,
+                                                   const uint16_t* Vl, float* D, LoadV&& load_v) {
+  constexpr int JB = NK <= 2 ? 4 : 2;      // 16-row blocks per wave and step
+  typedef typename MfmaOp<T>::vec vec;
+  constexpr int EPP = YPiece<TY>::EPP;
+  constexpr int WR = 64 * JB;              // output rows per step
+  constexpr int PPR = WR / EPP;            // pieces per token row of a step
+  constexpr int YP = 16 * PPR / kMT;       // pieces per thread
+  constexpr int DROW = WR + 4;             // accumulator staging row (floats)
+  static_assert(16 * DROW * 4 <= kDsB, "wide accumulator staging must fit D");
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int d_out = io.d_out;
+  const int m_end = min(64 * c1, d_out);   // rows of this range end here
+  const int rs = e.rs;
+  const float s = e.scale;
+  char* yrow[YP];
+  bool yok[YP];
+  int yslot[YP], ymo[YP];
+#pragma unroll
+  for (int j = 0; j < YP; ++j) {
+    const int q = t + kMT * j;
+    yslot[j] = q / PPR;
+    ymo[j] = (q % PPR) * EPP;
+    yok[j] = yslot[j] < count;
+    yrow[j] = reinterpret_cast<char*>(io.y) +
+              (int64_t)toks[min(yslot[j], count - 1)] * d_out * (int)sizeof(TY);
+  }
+  const int q_last = (d_out - 1) / e.rpp;
+  auto loadB = [&](int c, uint4 (&bo)[JB][NK]) {
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int mb0 = __builtin_amdgcn_readfirstlane(min(64 * c + 16 * JB * w + 16 * jb, d_out - 1));
+      const int m = min(mb0 + r16, d_out - 1);
+      const int64_t off = b_offset_wave(pv, e, 2, m, mb0, q_last);
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks)
+        bo[jb][ks] = ld16(pv.pages + off + (int64_t)min(32 * ks + 8 * g, rs - 8) * 2);
+    }
+  };
+  bool kok[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) kok[ks] = 32 * ks + 8 * g < rs;
+  auto loadY = [&](int c, uint4 (&yv)[YP]) {
+#pragma unroll
+    for (int j = 0; j < YP; ++j) {
+      const int m = min(64 * c + ymo[j], d_out - EPP);
+      yv[j] = ld16(yrow[j] + (int64_t)m * (int)sizeof(TY));
+    }
+  };
+  auto process = [&](int c, const uint4 (&bc)[JB][NK], const uint4 (&yc)[YP]) {
+    const int vo = r16 * kVpRow + 8 * g;
+    f32x4_t acc[JB];
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      const uint4 vh = *reinterpret_cast<const uint4*>(Vh + vo + 32 * ks);
+      const uint4 vl = *reinterpret_cast<const uint4*>(Vl + vo + 32 * ks);
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const vec bk = as_vec<vec>(keep16m(bc[jb][ks], kok[ks]));
+        acc[jb] = MfmaOp<T>::mma(bk, as_vec<vec>(vh), acc[jb]);
+        acc[jb] = MfmaOp<T>::mma(bk, as_vec<vec>(vl), acc[jb]);
+      }
+    }
+    lds_barrier();  // D is free: every wave is done with the previous step's RMW
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+      *reinterpret_cast<float4*>(D + r16 * DROW + 16 * JB * w + 16 * jb + 4 * g) =
+          make_float4(acc[jb][0], acc[jb][1], acc[jb][2], acc[jb][3]);
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < YP; ++j) {
+      const int m = 64 * c + ymo[j];
+      if (yok[j] && m < m_end) {
+        float a[EPP];
+        const float* dr = D + yslot[j] * DROW + ymo[j];
+#pragma unroll
+        for (int i = 0; i < EPP; i += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(dr + i);
+          a[i] = q.x;
+          a[i + 1] = q.y;
+          a[i + 2] = q.z;
+          a[i + 3] = q.w;
+        }
+        *reinterpret_cast<uint4*>(yrow[j] + (int64_t)m * (int)sizeof(TY)) = YPiece<TY>::fma(yc[j], a, s);
+      }
+    }
+  };
+  // Two register sets alternate by unrolling; prefetches past the range
+  // repeat its last step (clamped, never skipped).
+  const int cl = c0 + JB * ((c1 - c0 - 1) / JB);  // first chunk of the last step
+  uint4 b0[JB][NK], b1[JB][NK], y0[YP], y1[YP];
+  loadB(c0, b0);
+  loadY(c0, y0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v();
+  lds_barrier();  // V is in LDS
+  for (int c = c0; c < c1; c += 2 * JB) {
+    loadB(min(c + JB, cl), b1);
+    loadY(min(c + JB, cl), y1);
+    process(c, b0, y0);
+    loadB(min(c + 2 * JB, cl), b0);
+    loadY(min(c + 2 * JB, cl), y0);
+    if (c + JB < c1) process(c + JB, b1, y1);
+  }
+}
+
 // Fused: V of a tile from its contributors' partial tiles (summed in block
 // order, as the split API's reduce does) -> hi and lo parts in LDS.  Columns
 // [16 * ceil(rank / 16), 32 * NK) and slots past the count are zero.  A tile
@@ -696,30 +818,50 @@ __device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView&
     const int cb0 = off[0], cb1 = off[1];
     __syncthreads();
     switch ((e.rs + 31) >> 5) {
-      case 1:
-        expand_chunks<T, TY, 1>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
+      case 1: {
+        auto load_v = [&] {
           if constexpr (kFused) load_v_parts<T, 1>(pl, cb0, cb1, item.count, e.rank, Vh, Vl);
           else load_v_tile<T, 1>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
-        });
+        };
+        if (item.count <= 16)
+          expand_chunks_wide<T, TY, 1>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, load_v);
+        else
+          expand_chunks<T, TY, 1>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, load_v);
         break;
-      case 2:
-        expand_chunks<T, TY, 2>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
+      }
+      case 2: {
+        auto load_v = [&] {
           if constexpr (kFused) load_v_parts<T, 2>(pl, cb0, cb1, item.count, e.rank, Vh, Vl);
           else load_v_tile<T, 2>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
-        });
+        };
+        if (item.count <= 16)
+          expand_chunks_wide<T, TY, 2>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, load_v);
+        else
+          expand_chunks<T, TY, 2>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, load_v);
         break;
-      case 3:
-        expand_chunks<T, TY, 3>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
+      }
+      case 3: {
+        auto load_v = [&] {
           if constexpr (kFused) load_v_parts<T, 3>(pl, cb0, cb1, item.count, e.rank, Vh, Vl);
           else load_v_tile<T, 3>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
-        });
+        };
+        if (sizeof(TY) == 2 && item.count <= 16)  // (fp32 y: registers for the narrow steps only)
+          expand_chunks_wide<T, TY, 3>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, load_v);
+        else
+          expand_chunks<T, TY, 3>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, load_v);
         break;
-      default:
-        expand_chunks<T, TY, 4>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, [&] {
+      }
+      default: {
+        auto load_v = [&] {
           if constexpr (kFused) load_v_parts<T, 4>(pl, cb0, cb1, item.count, e.rank, Vh, Vl);
           else load_v_tile<T, 4>(v, v_ld, toks, item.count, e.rank, Vh, Vl);
-        });
+        };
+        if (sizeof(TY) == 2 && item.count <= 16)  // (fp32 y: registers for the narrow steps only)
+          expand_chunks_wide<T, TY, 4>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, load_v);
+        else
+          expand_chunks<T, TY, 4>(pv, e, io, toks, item.count, c0, c1, Vh, Vl, Ds, load_v);
         break;
+      }
     }
     lds_barrier();  // tokens and V are free (the y stores stay in flight)
   });

@@ -265,8 +265,13 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
       // a stage costs about one memory round trip whatever it moves: a large
       // fixed part plus half the rows
       ws[(size_t)i] = 64 + (16 * ((it.count + 15) / 16) + rp) / 2;
-      // an expand chunk: likewise a large fixed part, plus y and B rows
-      we[(size_t)i] = 256 + 2 * it.count + p->rs_of(rmax) / 2;
+      // an expand chunk (64 output rows), from per-chunk times measured on
+      // MI355X in units of ~4 ns: tiles of more than 16 tokens take 64-row
+      // steps, ~141 + 60 NK + 2 count; tiles of at most 16 tokens take wide
+      // steps (4 or 2 chunks, B of several chunks per round trip), ~51 + 51 NK
+      // + count per chunk (NK = 32-column k steps of the stored B row)
+      const int nk = (p->rs_of(rmax) + 31) / 32;
+      we[(size_t)i] = it.count <= 16 ? 51 + 51 * nk + it.count : 141 + 60 * nk + 2 * it.count;
       tu[(size_t)i] = (rp / 16) * ((it.count + 15) / 16) * 64;
     }
   }
