@@ -304,12 +304,6 @@ void apply_launch(const PoolView& pv, const IoSet& ios, const int32_t* ids, int 
     hipLaunchKernelGGL((k_bgmv_apply<T, TY, NT, U, 8>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
 }
 
-// Launch-shape overrides for tuning sweeps (0: automatic).
-inline int env_int(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
-}
-
 template <typename T, typename TY>
 hipError_t apply_t(const PoolView& pv, const IoSet& ios_in, const int32_t* ids, int n,
                    hipStream_t s) {
@@ -321,22 +315,15 @@ hipError_t apply_t(const PoolView& pv, const IoSet& ios_in, const int32_t* ids, 
     return a.d_in + a.d_out > b.d_in + b.d_out;
   });
   const int units = n * ios.n_io;
-  static const int force_split = env_int("LORA_BGMV_SPLIT");
-  static const int force_nt = env_int("LORA_BGMV_NT");
   // Splitting a unit repeats its whole shrink, which costs more than it
-  // gains (measured); split only when there are fewer units than CUs.
+  // gains (measured, also when only the units with the largest B are split);
+  // split only when there are fewer units than CUs.
   int nsplit = 1;
-  if (force_split > 0) {
-    nsplit = force_split;
-  } else {
-    while ((long)units * nsplit < 256 && ios.max_d_out / (nsplit * 2) >= 512) nsplit *= 2;
-  }
+  while ((long)units * nsplit < 256 && ios.max_d_out / (nsplit * 2) >= 512) nsplit *= 2;
   const int rps = (((ios.max_d_out + nsplit - 1) / nsplit) + 63) & ~63;
   const dim3 grid(xcd_grid(units, nsplit));
   const int C = ios.max_d_in / E;
-  if (force_nt == 256 && C <= 512) {
-    apply_launch<T, TY, 256, 2>(pv, ios, ids, n, grid, nsplit, rps, s);
-  } else if (C >= 512) {
+  if (C >= 512) {
     if (pick_u(ios.max_d_in, E, 512) == 1)
       apply_launch<T, TY, 512, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
     else
