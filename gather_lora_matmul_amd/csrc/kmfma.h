@@ -6,7 +6,7 @@
 // shape the host splits the launch's work sequence (the tiles of launch slice
 // 0, then of slice 1, ...; stages or chunks weighted by the bytes they move)
 // into one contiguous range per block (layout.h), so every block moves about
-// the same number of bytes and no block waits in a second round.
+// the same number of bytes and no block waits for a second wave of the grid.
 //
 // Shrink  V^T[n][t] = sum_j A[n][j] X[t][j]   (M = rank, N = tokens, K = d_in)
 //   Stages of 64 columns: the X rows of the tile's tokens and the A rows of

@@ -182,12 +182,15 @@ typedef struct {
   int32_t l_long;       /* group length from which MFMA tiles are used           */
 } lora_plan_stats;
 
-/* Plan for up to max_tokens tokens (device buffers allocated once; on 16-bit
- * pools the MFMA tiles' shrink also needs a workspace of partial tiles, about
- * 4 bytes per token and rank unit per slice of a launch plus the tile
- * boundaries, grown at first use).  A plan is used by one stream at a time:
- * launches that use the same plan must not overlap (they share its
- * workspace). */
+/* Plan for up to max_tokens tokens (perm and item buffers allocated here).
+ * On 16-bit pools the MFMA tiles also need, per launch shape (the slices of a
+ * call), block-range tables and split-K contribution lists -- built on the
+ * host at the first call of that shape after lora_plan_build and copied on the
+ * call's stream; the plan keeps four shapes -- and a workspace of partial
+ * tiles (16 bytes per token block x rank block x 64 per contribution, a few
+ * MB), grown at first use (growing synchronizes the device).  A plan is used
+ * by one stream at a time: calls that use the same plan must not overlap
+ * (they share its workspace). */
 lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** out);
 lora_status lora_plan_destroy(lora_plan* plan);
 /* Build the plan of one batch from host ids [n] (any order, -1 = no adapter):
@@ -208,7 +211,9 @@ lora_status lora_plan_get_stats(const lora_plan* plan, lora_plan_stats* out);
 lora_status lora_plan_export(const lora_plan* plan, int32_t* perm_host, int32_t* items_host);
 
 /* Shrink for a planned batch: v[i][.] as lora_bgmv_shrink (rows indexed by the
- * original token index). */
+ * original token index).  MFMA tiles: two launches (block ranges, then the sum
+ * of the partial tiles of every tile that several ranges share, in block
+ * order). */
 lora_status lora_sgmv_shrink(lora_pool* pool, const lora_plan* plan, int32_t slice,
                              const void* x_dev, float* v_dev, int32_t v_ld, void* stream);
 /* Expand for a planned batch: y[i] += s B v[i]. */
