@@ -241,6 +241,10 @@ SMALL_SGMV = [
     # pages large enough for every rank on MFMA tiles; A rows over two pages
     ("bf16", 2304, 1000, [128, 16, 64, 5, 96], 2048,
      [0] * 150 + [1] * 65 + [2] * 7 + [3] * 1 + [4] * 40 + [-1] * 3),
+    # groups of at most 16 tokens at every rank band (wide expand steps of 4 and
+    # 2 chunks), d_out not a multiple of a step, plus one large group
+    ("bf16", 2048, 1000, [128, 96, 64, 33, 8, 16], 2048,
+     [0] * 5 + [1] * 16 + [2] * 9 + [3] * 1 + [4] * 12 + [0] * 3 + [5] * 80 + [-1] * 2),
 ]
 
 
