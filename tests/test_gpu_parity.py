@@ -318,6 +318,54 @@ def test_sgmv_plan_reuse_repeated_launches():
             assert outs[rep][s].tobytes() == outs[0][s].tobytes(), "launch %d differs" % rep
 
 
+def test_plan_layouts_across_launch_shapes():
+    """One plan, calls over more distinct launch shapes (slice sets) than the
+    plan keeps layouts for: every call matches the oracle, and a shape that
+    comes back after its layout was evicted gives bit-identical results."""
+    log("[case] plan layouts across launch shapes")
+    shapes = [(256, 256), (512, 264), (256, 520), (768, 256), (512, 512), (256, 1000)]
+    ranks = np.array([16, 40, 8, 64, 33], np.int32)
+    wl = W.Workload("custom", "bgmv", "bf16", 1024, shapes, ranks,
+                    np.array([16.0 / r for r in ranks], np.float32), 77, shuffle_seed=11,
+                    pool_slack=2.0, kv_dummy_ratio=0.0)
+    ids = np.array([0] * 70 + [1] * 9 + [2] * 33 + [3] * 3 + [4] * 20 + [-1] * 2, np.int32)
+    np.random.default_rng(5).shuffle(ids)
+    b = W.custom_batch(wl, ids, zero_y0=True)
+    sp = pool_for(("layouts",), wl)
+    n = len(ids)
+    plan = L.lora_plan_create(sp.handle, n)
+    try:
+        L.lora_plan_build(plan, ids)
+        xs = [to_device(b.x[s], "bf16") for s in range(len(shapes))]
+        refs = {}
+        first = {}
+        sets = [[0], [1], [0, 2], [3], [4, 5], [1, 2, 3], [0], [5], [0, 2], [2, 4, 5, 1]]
+        for k, sl in enumerate(sets):
+            ys = [Guarded(b.y0[s], "bf16") for s in sl]
+            if k % 3 == 2:  # split calls share the layout of their single slice
+                v_ld = sp.max_rank
+                for j, s in enumerate(sl):
+                    v = Guarded(np.full((n, v_ld), np.nan, np.float32), "f32")
+                    L.lora_sgmv_shrink(sp.handle, plan, s, xs[s], v.view, v_ld)
+                    L.lora_sgmv_expand(sp.handle, plan, s, v.view, ys[j].view, L.LORA_BF16, v_ld=v_ld)
+                    v.host()
+            else:
+                L.lora_apply(sp.handle, plan, [(s, xs[s], ys[j].view) for j, s in enumerate(sl)],
+                             L.LORA_BF16)
+            torch.cuda.synchronize()
+            for j, s in enumerate(sl):
+                got = ys[j].host()
+                if s not in refs:
+                    refs[s] = reference(wl, b, s, "bf16")
+                compare(got, refs[s], "bf16", "layouts call %d slice %d" % (k, s))
+                key = (tuple(sl), s, k % 3 == 2)
+                if key in first:
+                    assert np.array_equal(first[key], got), "call %d slice %d not bit-identical" % (k, s)
+                first.setdefault(key, got)
+    finally:
+        L.lora_plan_destroy(plan)
+
+
 def test_sgmv_llama13b_prefill_full():
     wl = W.make_workload(3)
     b = W.make_batch(wl, 0)
