@@ -37,26 +37,87 @@ void for_pieces(Pos a, Pos b, int T, const std::vector<int32_t>& n, F&& f) {
 
 }  // namespace
 
-void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G,
+namespace {
+
+void set_pos(int32_t* out, int L, int j, int t, int k) {
+  int32_t* o = out + kPosInts * L;
+  o[0] = j;
+  o[1] = t;
+  o[2] = k;
+  o[3] = 0;
+}
+
+// Blocks needed when each takes units in sequence until its cost (units times
+// their weight, plus ov for every tile piece it touches) would pass `cap`; a
+// block always takes at least one unit.  Stops counting past G.  out (if
+// given): the start of every used block.
+int greedy_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G, int64_t ov,
+                  int64_t cap, int32_t* out) {
+  const int T = (int)w.size(), J = (int)n.size();
+  int used = 0;
+  bool open = false;
+  int64_t cost = 0;
+  for (int j = 0; j < J; ++j)
+    for (int t = 0; t < T; ++t) {
+      const int64_t nn = n[(size_t)j], wt = w[(size_t)t];
+      int64_t k = 0;
+      while (k < nn) {
+        if (!open) {
+          if (used == G) return G + 1;
+          if (out) set_pos(out, used, j, t, (int)k);
+          ++used;
+          open = true;
+          cost = 0;
+        }
+        const int64_t avail = cap - cost - ov;
+        int64_t take = avail >= wt ? std::min(nn - k, avail / wt) : 0;
+        if (take == 0) {
+          if (cost > 0) {  // full: the next block starts here
+            open = false;
+            continue;
+          }
+          take = 1;
+        }
+        cost += ov + take * wt;
+        k += take;
+        if (k < nn) open = false;  // full inside the tile
+      }
+    }
+  return used;
+}
+
+}  // namespace
+
+void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G, int64_t ov,
                     int32_t* out) {
   const int T = (int)w.size(), J = (int)n.size();
   int64_t per = 0, total = 0;
   for (int32_t x : w) per += x;
   for (int32_t nj : n) total += per * nj;
+  if (ov > 0 && (int64_t)J * T <= kMaxPiecesOv) {
+    // smallest per-block cap that G blocks cover (binary search)
+    int64_t wmax = 0;
+    for (int32_t x : w) wmax = std::max<int64_t>(wmax, x);
+    int64_t lo = std::max<int64_t>(1, total / G), hi = total + ov * (int64_t)J * T + ov + wmax;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (greedy_ranges(w, n, G, ov, mid, nullptr) <= G) hi = mid;
+      else lo = mid + 1;
+    }
+    const int used = greedy_ranges(w, n, G, ov, lo, out);
+    for (int L = used; L <= G; ++L) set_pos(out, L, J, 0, 0);
+    return;
+  }
   int j = 0, t = 0;
   int64_t before = 0;  // weight of the units before tile t of slice j
   for (int L = 0; L <= G; ++L) {
     const int64_t target = total * L / G;
-    int32_t* o = out + kPosInts * L;
-    o[0] = J;
-    o[1] = o[2] = o[3] = 0;
+    set_pos(out, L, J, 0, 0);
     while (j < J) {
       const int64_t wt = w[(size_t)t];
       const int64_t k = std::max<int64_t>(0, (target - before + wt - 1) / wt);
       if (k < n[(size_t)j]) {
-        o[0] = j;
-        o[1] = t;
-        o[2] = (int32_t)k;
+        set_pos(out, L, j, t, (int)k);
         break;
       }
       before += wt * n[(size_t)j];
@@ -70,7 +131,8 @@ void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n
 
 bool layout_host(const std::vector<int32_t>& ws, const std::vector<int32_t>& we,
                  const std::vector<int32_t>& tu, const std::vector<int32_t>& nst,
-                 const std::vector<int32_t>& nch, int G, LayoutHost& h) {
+                 const std::vector<int32_t>& nch, int G, int64_t ov_s, int64_t ov_e,
+                 LayoutHost& h) {
   const int J = (int)nst.size();
   const int T = (int)ws.size();
   h.o_bs = 0;
@@ -80,8 +142,8 @@ bool layout_host(const std::vector<int32_t>& ws, const std::vector<int32_t>& we,
   h.o_ent = (h.o_off + (size_t)J * ((size_t)T + 1) + 3) & ~(size_t)3;
   std::vector<int32_t>& buf = h.buf;
   buf.assign(h.o_ent, 0);
-  balance_ranges(ws, nst, G, buf.data() + h.o_bs);
-  balance_ranges(we, nch, G, buf.data() + h.o_be);
+  balance_ranges(ws, nst, G, ov_s, buf.data() + h.o_bs);
+  balance_ranges(we, nch, G, ov_e, buf.data() + h.o_be);
   // per (j, tile) the blocks whose shrink ranges meet it, in block order; each
   // block's first and last piece
   std::vector<std::vector<int32_t>> lists((size_t)J * (size_t)T);

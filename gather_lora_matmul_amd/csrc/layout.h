@@ -17,9 +17,14 @@ namespace lora {
 // Positions are normalized: k < n[j], tile < T, j < J, or the end {J, 0, 0}.
 constexpr int kPosInts = 4;
 
-// Block L's range is [pos[L], pos[L + 1]): pos[L] is the first unit whose
-// cumulative start weight is at least total * L / G.  out: (G + 1) positions.
-void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G,
+// Block L's range is [pos[L], pos[L + 1]); out: (G + 1) positions.  ov == 0:
+// pos[L] is the first unit whose cumulative start weight is at least
+// total * L / G.  ov > 0: a block also pays ov for every tile piece it touches
+// (its per-tile set-up); ranges are cut greedily under the smallest per-block
+// cap that G blocks cover, so blocks that touch more tiles get fewer units
+// (sequences of more than kMaxPiecesOv tiles fall back to ov == 0).
+constexpr int64_t kMaxPiecesOv = 16384;
+void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G, int64_t ov,
                     int32_t* out);
 
 // The int32 image of a launch shape's layout, copied to the device as is:
@@ -37,9 +42,11 @@ struct LayoutHost {
   int64_t part_units = 0;  // float4 units of all partial tiles
 };
 
-// False if the partial tiles would exceed 2^31 float4 units.
+// ov_s, ov_e: per-piece set-up cost of the shrink and expand ranges (in the
+// units of ws, we).  False if the partial tiles would exceed 2^31 float4 units.
 bool layout_host(const std::vector<int32_t>& ws, const std::vector<int32_t>& we,
                  const std::vector<int32_t>& tu, const std::vector<int32_t>& nst,
-                 const std::vector<int32_t>& nch, int G, LayoutHost& h);
+                 const std::vector<int32_t>& nch, int G, int64_t ov_s, int64_t ov_e,
+                 LayoutHost& h);
 
 }  // namespace lora

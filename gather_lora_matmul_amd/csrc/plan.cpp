@@ -22,6 +22,12 @@ static_assert(sizeof(RangePos) == kPosInts * sizeof(int32_t), "device positions 
 
 namespace lora {
 
+// Set-up of one tile piece of a block range, in the weight units below
+// (measured: ~5 us for a shrink piece -- tokens, A page ids, pipeline fill --
+// and ~6 us for an expand piece -- tokens, V from the partial tiles, fill).
+constexpr int64_t kPieceSetupShrink = 600;
+constexpr int64_t kPieceSetupExpand = 1800;
+
 lora_status plan_layout(lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out) {
   const int J = ios.n_io;
   const int T = pl->n_mfma;
@@ -45,7 +51,8 @@ lora_status plan_layout(lora_plan* pl, const IoSet& ios, hipStream_t s, const Pl
       if (!l.valid || l.used < lay->used) lay = &l;
     lay->valid = false;
     LayoutHost h;
-    if (!layout_host(pl->h_ws, pl->h_we, pl->h_tu, nst, nch, G, h))
+    if (!layout_host(pl->h_ws, pl->h_we, pl->h_tu, nst, nch, G, kPieceSetupShrink,
+                     kPieceSetupExpand, h))
       return fail(LORA_E_ARG, "plan: partial-tile workspace exceeds 2^31 float4 units");
     const std::vector<int32_t>& buf = h.buf;
     const int64_t units = h.part_units;

@@ -1,10 +1,12 @@
 // Host check of the persistent MFMA kernels' block ranges (layout.cpp): on
 // seeded random launch shapes, every unit of the work sequence belongs to
-// exactly one block, positions are normalized and monotone, the weight of a
-// block's range is within one unit of the mean, and replaying the kernels'
-// walk (first / last piece flags, as for_each_piece in kmfma.h computes them)
-// finds each piece's partial tile at the offset listed for that block in the
-// tile's contributions, in block order, with disjoint offsets.
+// exactly one block, positions are normalized and monotone; without a piece
+// set-up cost the weight of a block's range is within one unit of the mean,
+// with one the largest block cost (weights plus set-up per piece) is no larger
+// than under the plain split; and replaying the kernels' walk (first / last
+// piece flags, as for_each_piece in kmfma.h computes them) finds each piece's
+// partial tile at the offset listed for that block in the tile's
+// contributions, in block order, with disjoint offsets.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
@@ -42,8 +44,10 @@ int main(int argc, char** argv) {
       nst[j] = 1 + rng() % ((trial % 5 == 0) ? 3 : 400);
       nch[j] = 1 + rng() % 400;
     }
+    const int64_t ov_s = (trial % 2) ? 0 : 1 + rng() % 2000;
+    const int64_t ov_e = (trial % 4 == 1) ? 0 : 1 + rng() % 3000;
     LayoutHost h;
-    if (!lora::layout_host(ws, we, tu, nst, nch, G, h)) {
+    if (!lora::layout_host(ws, we, tu, nst, nch, G, ov_s, ov_e, h)) {
       fail("layout_host refused", trial);
       continue;
     }
@@ -54,6 +58,8 @@ int main(int argc, char** argv) {
       const int32_t* tab = h.buf.data() + (pass ? h.o_be : h.o_bs);
       const std::vector<int32_t>& n = pass ? nch : nst;
       const std::vector<int32_t>& w = pass ? we : ws;
+      const int64_t ov = pass ? ov_e : ov_s;
+      double max_cost = 0;
       std::vector<std::vector<int>> cover((size_t)J * T);
       for (int j = 0; j < J; ++j)
         for (int t = 0; t < T; ++t) cover[(size_t)j * T + t].assign(n[j], 0);
@@ -70,7 +76,7 @@ int main(int argc, char** argv) {
         // the kernels' walk
         int j = a.j, t = a.t, k = a.k;
         bool first = true;
-        double wsum = 0;
+        double wsum = 0, cost = 0;
         while (lt(P{j, t, k}, b)) {
           const bool ends_here = j == b.j && t == b.t;
           const int k1 = ends_here ? b.k : n[j];
@@ -83,6 +89,7 @@ int main(int argc, char** argv) {
           if (!(k < k1)) fail("empty piece", trial);
           for (int kk = k; kk < k1; ++kk) cover[(size_t)j * T + t][kk]++;
           wsum += (double)(k1 - k) * w[t];
+          cost += (double)(k1 - k) * w[t] + ov;
           if (pass == 0) {
             const int32_t off = first ? fl[2 * L] : last ? fl[2 * L + 1] : cent[coff[j * (T + 1) + t]];
             // block L's index among the tile's contributors (blocks whose
@@ -104,7 +111,30 @@ int main(int argc, char** argv) {
           t = nt;
           k = 0;
         }
-        if (wsum > total / G + wmax + 1e-6) fail("imbalance", trial);
+        if (ov == 0 && wsum > total / G + wmax + 1e-6) fail("imbalance", trial);
+        max_cost = std::max(max_cost, cost);
+      }
+      if (ov > 0 && (int64_t)J * T <= lora::kMaxPiecesOv) {
+        // the plain split (no set-up cost) under the same cost: never better
+        std::vector<int32_t> plain((size_t)kPosInts * (G + 1));
+        lora::balance_ranges(w, n, G, 0, plain.data());
+        double plain_max = 0;
+        for (int L = 0; L < G; ++L) {
+          const P a = at(plain.data(), L), b = at(plain.data(), L + 1);
+          double c = 0;
+          int j = a.j, t = a.t, k = a.k;
+          while (lt(P{j, t, k}, b)) {
+            const int k1 = (j == b.j && t == b.t) ? b.k : n[j];
+            c += (double)(k1 - k) * w[t] + ov;
+            k = 0;
+            if (++t == T) {
+              t = 0;
+              ++j;
+            }
+          }
+          plain_max = std::max(plain_max, c);
+        }
+        if (max_cost > plain_max + 1e-6) fail("set-up-aware split worse than the plain one", trial);
       }
       for (auto& c : cover)
         for (int x : c)
