@@ -541,7 +541,8 @@ __device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry
   // Three register sets rotate by unrolling (a register copy of a load in
   // flight would wait for it): chunk c uses set (c - c0) % 3, and the loads of
   // chunk c + 2 are issued before chunk c is computed.  Prefetches are never
-  // skipped (see shrink_stages): past c1 they repeat the last chunk.
+  // skipped (register loads under a branch compile to a wait right behind
+  // them): past c1 they repeat the last chunk.
   auto process = [&](int c, const uint4 (&bc)[NK], const uint4 (&yc)[YP]) {
     f32x4_t acc[4];
 #pragma unroll
