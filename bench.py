@@ -114,6 +114,9 @@ def main():
                              "llama70b_mixed_apply"])
     ap.add_argument("--batches", type=int, default=None,
                     help="rotating batches (default 16 for decode, 4 for planned batches)")
+    ap.add_argument("--planned", action="store_true",
+                    help="decode workloads: plan each batch on the host and run lora_apply "
+                         "(the SGMV path) instead of lora_bgmv_apply")
     ap.add_argument("--l-long", type=int, default=0,
                     help="planned batches: groups shorter than this run as short VALU items "
                          "(0: every group of a 16-bit pool is an MFMA tile)")
@@ -136,7 +139,7 @@ def main():
     cfg = {"llama7b_decode_bgmv": 1, "hetero_decode_bgmv": 2, "llama13b_prefill_sgmv": 3,
            "llama70b_mixed_apply": 4}[args.workload]
     wl = W.make_workload(cfg)
-    planned = cfg >= 3
+    planned = cfg >= 3 or args.planned
     slices = list(range(len(wl.slices)))
     n_batches = args.batches or (4 if planned else 16)
     print("[bench] building pool: %s, %d adapters x %d slices" % (wl.name, wl.n_adapters, len(slices)),
@@ -199,7 +202,7 @@ def main():
     avg_bytes = float(np.mean(used))
     avg_kernel_s = float(np.mean(kern_ms)) * 1e-3
     achieved = avg_bytes / avg_kernel_s / 1e9
-    traffic = measured_traffic() if args.mode == "fused" and cfg == 1 else None
+    traffic = measured_traffic() if args.mode == "fused" and cfg == 1 and not planned else None
     if args.copy_calib:
         src = torch.empty(64 << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
