@@ -139,7 +139,7 @@ lora_status lora_sgmv_shrink(lora_pool* p, const lora_plan* pl, int32_t slice, c
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
   const IoDesc io = p->io(slice, x, nullptr);
   const PlanLayout* lay = nullptr;
-  if (pl->n_mfma > 0) LORA_TRY(plan_layout(const_cast<lora_plan*>(pl), single_io(io), (hipStream_t)stream, &lay));
+  if (pl->n_mfma > 0) LORA_TRY(plan_layout(pl, single_io(io), (hipStream_t)stream, &lay));
   return hip_status(launch_sgmv_shrink(p->dtype, p->view(), pl->view(lay), io, v, v_ld, (hipStream_t)stream),
                     "sgmv_shrink");
 }
@@ -157,7 +157,7 @@ lora_status lora_sgmv_expand(lora_pool* p, const lora_plan* pl, int32_t slice, c
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
   const IoDesc io = p->io(slice, nullptr, y);
   const PlanLayout* lay = nullptr;
-  if (pl->n_mfma > 0) LORA_TRY(plan_layout(const_cast<lora_plan*>(pl), single_io(io), (hipStream_t)stream, &lay));
+  if (pl->n_mfma > 0) LORA_TRY(plan_layout(pl, single_io(io), (hipStream_t)stream, &lay));
   return hip_status(launch_sgmv_expand(p->dtype, y_dtype, p->view(), pl->view(lay), io, v, v_ld,
                                        (hipStream_t)stream),
                     "sgmv_expand");
@@ -173,7 +173,7 @@ lora_status lora_apply(lora_pool* p, const lora_plan* pl, int32_t n_io, const lo
   LORA_TRY(build_ioset(p, n_io, io, ios));
   if (pl->n_tokens == 0) return LORA_OK;
   const PlanLayout* lay = nullptr;
-  if (pl->n_mfma > 0) LORA_TRY(plan_layout(const_cast<lora_plan*>(pl), ios, (hipStream_t)stream, &lay));
+  if (pl->n_mfma > 0) LORA_TRY(plan_layout(pl, ios, (hipStream_t)stream, &lay));
   return hip_status(launch_apply(p->dtype, y_dtype, p->view(), pl->view(lay), ios, (hipStream_t)stream),
                     "apply");
 }

@@ -28,7 +28,7 @@ namespace lora {
 constexpr int64_t kPieceSetupShrink = 600;
 constexpr int64_t kPieceSetupExpand = 1800;
 
-lora_status plan_layout(lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out) {
+lora_status plan_layout(const lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out) {
   const int J = ios.n_io;
   const int T = pl->n_mfma;
   const int G = pl->G;

@@ -117,7 +117,7 @@ constexpr int kPlanLayouts = 4;
 
 // Layout for the launch slices of `ios` (built and uploaded on `s` if the plan
 // has none of that shape), with the plan's partial-tile workspace grown to it.
-lora_status plan_layout(lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out);
+lora_status plan_layout(const lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out);
 }  // namespace lora
 
 struct lora_plan {
@@ -144,10 +144,12 @@ struct lora_plan {
   std::vector<int32_t> h_ws;  // per MFMA tile: weight of one shrink stage
   std::vector<int32_t> h_we;  //   ... of one expand chunk
   std::vector<int32_t> h_tu;  //   ... float4 units of one partial tile
-  lora::PlanLayout layouts[lora::kPlanLayouts];
-  uint64_t layout_clock = 0;
-  float* d_part = nullptr;    // partial tiles, grown on demand
-  size_t part_cap = 0;        // floats
+  // Launch-time state of a built plan (compute calls take the plan as const):
+  // the cache of launch-shape layouts and the partial-tile workspace.
+  mutable lora::PlanLayout layouts[lora::kPlanLayouts];
+  mutable uint64_t layout_clock = 0;
+  mutable float* d_part = nullptr;  // partial tiles, grown on demand
+  mutable size_t part_cap = 0;      // floats
   lora::PlanView view(const lora::PlanLayout* lay) const {
     lora::PlanView v;
     v.items = d_items;

@@ -189,8 +189,8 @@ typedef struct {
  * call's stream; the plan keeps four shapes -- and a workspace of partial
  * tiles (16 bytes per token block x rank block x 64 per contribution, a few
  * MB), grown at first use (growing synchronizes the device).  A plan is used
- * by one stream at a time: calls that use the same plan must not overlap
- * (they share its workspace). */
+ * by one stream and one host thread at a time: calls that use the same plan
+ * must not overlap (they share its workspace and layout cache). */
 lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** out);
 lora_status lora_plan_destroy(lora_plan* plan);
 /* Build the plan of one batch from host ids [n] (any order, -1 = no adapter):
