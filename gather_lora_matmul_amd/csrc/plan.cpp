@@ -254,9 +254,10 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
   for (const Keyed& k : items) pl->h_items.push_back(k.it);
   {
     // Weights of the MFMA tiles (items [0, n_mfma)) per shrink stage and per
-    // expand chunk, in 128-byte rows moved, and the size of a partial tile.
-    // The range tables and contributions are built per launch shape
-    // (plan_layout); the plan's old ones are dropped here.
+    // expand chunk (each in its own unit, consistent with the per-piece set-up
+    // costs of plan_layout), and the size of a partial tile.  The range tables
+    // and contributions are built per launch shape (plan_layout); the plan's
+    // old ones are dropped here.
     std::vector<int32_t>& ws = pl->h_ws;
     std::vector<int32_t>& we = pl->h_we;
     std::vector<int32_t>& tu = pl->h_tu;
@@ -270,7 +271,7 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
       for (int s = 0; s < p->n_slices; ++s) rmax = std::max(rmax, p->slot(s, it.adapter).rank);
       const int rp = (rmax + 15) / 16 * 16;
       // a stage costs about one memory round trip whatever it moves: a large
-      // fixed part plus half the rows
+      // fixed part plus half the 128-byte rows it loads (units of ~8 ns)
       ws[(size_t)i] = 64 + (16 * ((it.count + 15) / 16) + rp) / 2;
       // an expand chunk (64 output rows), from per-chunk times measured on
       // MI355X in units of ~4 ns: tiles of more than 16 tokens take 64-row
