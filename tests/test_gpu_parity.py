@@ -318,6 +318,69 @@ def test_sgmv_plan_reuse_repeated_launches():
             assert outs[rep][s].tobytes() == outs[0][s].tobytes(), "launch %d differs" % rep
 
 
+def test_empty_batches_and_tokens_without_adapters():
+    """Empty batches: every entry point returns and writes nothing.  A batch in
+    which no token has an adapter leaves y bit-identical (BGMV and planned)."""
+    log("[case] empty batches, all ids -1")
+    wl = W.small_workload("bf16", 512, 264, [8, 40, 16], 256, n_slices=2, seed=9)
+    sp = pool_for(("edge",), wl)
+    n = 37
+    b = W.custom_batch(wl, np.full(n, -1, np.int32))  # random y0
+    x = to_device(b.x[0], "bf16")
+    y = Guarded(b.y0[0], "bf16")
+    v = Guarded(np.full((n, sp.max_rank), np.nan, np.float32), "f32")
+    plan = L.lora_plan_create(sp.handle, n)
+    try:
+        L.lora_bgmv_apply(sp.handle, [(0, x, y.view)], ids_tensor(np.zeros(0, np.int32)), L.LORA_BF16)
+        L.lora_plan_build(plan, np.zeros(0, np.int32))
+        L.lora_apply(sp.handle, plan, [(0, x, y.view)], L.LORA_BF16)
+        L.lora_sgmv_shrink(sp.handle, plan, 0, x, v.view, sp.max_rank)
+        L.lora_sgmv_expand(sp.handle, plan, 0, v.view, y.view, L.LORA_BF16, v_ld=sp.max_rank)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.host(), b.y0[0])
+        assert np.all(np.isnan(v.host())), "an empty plan wrote v"
+        L.lora_bgmv_apply(sp.handle, [(0, x, y.view)], ids_tensor(b.ids), L.LORA_BF16)
+        L.lora_plan_build(plan, b.ids)
+        L.lora_apply(sp.handle, plan, [(0, x, y.view)], L.LORA_BF16)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.host(), b.y0[0])
+    finally:
+        L.lora_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("entry", ["bgmv", "planned"])
+def test_fused_apply_max_slices(entry):
+    """LORA_MAX_IO (8) slices in one fused call match the oracle; a ninth is
+    refused before anything is written."""
+    log("[case] fused apply with 8 slices (%s)" % entry)
+    wl = W.small_workload("f16", 256, 520, [8, 16, 33], 256, n_slices=9, seed=10)
+    sp = pool_for(("max_io",), wl)
+    ids = np.array([0, 2, -1, 1, 1, 0, 2, 2, 1, 0, 2] * 3, np.int32)
+    b = W.custom_batch(wl, ids, zero_y0=True)
+    xs = [to_device(b.x[s], "f16") for s in range(9)]
+    ys = [Guarded(b.y0[s], "f16") for s in range(9)]
+    plan = L.lora_plan_create(sp.handle, len(ids)) if entry == "planned" else None
+    try:
+        def call(k):
+            io = [(s, xs[s], ys[s].view) for s in range(k)]
+            if plan is None:
+                L.lora_bgmv_apply(sp.handle, io, ids_tensor(ids), L.LORA_F16)
+            else:
+                L.lora_apply(sp.handle, plan, io, L.LORA_F16)
+        if plan is not None:
+            L.lora_plan_build(plan, ids)
+        with pytest.raises(L.LoraError):
+            call(9)
+        call(8)
+        torch.cuda.synchronize()
+        for s in range(8):
+            compare(ys[s].host(), reference(wl, b, s, "f16"), "f16", "max slices %s s%d" % (entry, s))
+        assert np.array_equal(ys[8].host(), b.y0[8])
+    finally:
+        if plan is not None:
+            L.lora_plan_destroy(plan)
+
+
 def test_plan_layouts_across_launch_shapes():
     """One plan, calls over more distinct launch shapes (slice sets) than the
     plan keeps layouts for: every call matches the oracle, and a shape that
