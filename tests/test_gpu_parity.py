@@ -267,6 +267,24 @@ def test_sgmv_small(case, mode, l_long):
         compare(ys[s], reference(wl, b, s, dtype), dtype, "sgmv small %d s%d" % (case, s))
 
 
+@pytest.mark.parametrize("case", [0, 3, 4])
+@pytest.mark.parametrize("mode", ["split", "fused"])
+def test_sgmv_f32_output(case, mode):
+    """16-bit pool, fp32 y (accumulated from a random y0): the MFMA tiles'
+    fp32-output expand (64-row and wide steps) against the unrounded oracle."""
+    dtype, d_in, d_out, ranks, P, ids = SMALL_SGMV[case]
+    log("[case] sgmv small %d f32 y mode=%s" % (case, mode))
+    wl = W.small_workload(dtype, d_in, d_out, ranks, P, n_slices=2, seed=40 + case)
+    ids = np.array(ids, np.int32)
+    np.random.default_rng(100 + case).shuffle(ids)
+    b = W.custom_batch(wl, ids, y_dtype="f32", zero_y0=False)
+    sp = pool_for(("small", case), wl)
+    ys, st = run_sgmv(sp, b, [0, 1], "f32", mode)
+    assert st["n_mfma_items"] > 0
+    for s_ in range(2):
+        compare(ys[s_], reference(wl, b, s_, "f32"), "f32", "sgmv small %d f32 s%d" % (case, s_))
+
+
 @pytest.mark.parametrize("mode", ["split", "fused"])
 def test_sgmv_exact_small_bit_exact(mode):
     wl = W.small_workload("bf16", 512, 328, [16, 64, 5, 128, 33], 256, n_slices=1, exact=True, seed=77)
