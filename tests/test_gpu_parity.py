@@ -470,11 +470,29 @@ def test_mixed_llama70b_full():
     rng = np.random.default_rng(6)
     sub = np.sort(np.concatenate([rng.choice(4096, 96, replace=False),
                                   4096 + rng.choice(512, 64, replace=False)]))
-    ys, st = run_sgmv(sp, b, [0, 1], wl.dtype, "fused")
+    for mode in ("split", "fused"):
+        ys, st = run_sgmv(sp, b, [0, 1], wl.dtype, mode)
+        assert st["n_mfma_items"] > 0
+        for s in range(2):
+            compare(ys[s][sub], reference(wl, b, s, wl.dtype, subset=sub), wl.dtype,
+                    "cfg4 %s s%d (sampled tokens)" % (mode, s))
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("mode", ["split", "fused"])
+def test_planned_decode_batches_full(cfg, mode):
+    # The decode batches with their ids known on the host, run as a plan: every
+    # adapter group (one token each, or up to 16 in the heterogeneous batch)
+    # becomes an MFMA tile on the wide expand steps; every token checked.
+    wl = W.make_workload(cfg)
+    b = W.make_batch(wl, 0)
+    slices = list(range(len(wl.slices)))
+    log("[case] planned decode cfg=%d mode=%s, %d tokens" % (cfg, mode, len(b.ids)))
+    sp = pool_for("cfg%d" % cfg, wl)
+    ys, st = run_sgmv(sp, b, slices, wl.dtype, mode)
     assert st["n_mfma_items"] > 0
-    for s in range(2):
-        compare(ys[s][sub], reference(wl, b, s, wl.dtype, subset=sub), wl.dtype,
-                "cfg4 fused s%d (sampled tokens)" % s)
+    for s in slices:
+        compare(ys[s], reference(wl, b, s, wl.dtype), wl.dtype, "planned cfg%d %s s%d" % (cfg, mode, s))
 
 
 @pytest.mark.parametrize("cfg", [3, 4])
