@@ -88,13 +88,12 @@ constexpr int kMT = 256;                       // threads per block
 constexpr int kKC = 64;                        // shrink stage: columns of X and A
 constexpr int kRowB = kKC * 2;                 // staged row: 128 bytes (swizzled units)
 constexpr int kStageB = (kTileM + kMaxR) * kRowB;  // X rows, then A rows
-constexpr int kVpRow = kMaxR + 8;              // packed V half-row (uint16): hi or lo, pad
 constexpr int kDsRow = 64 + 4;                 // accumulator staging row (floats)
 constexpr int kOffToks = 0;                    // misc: int[64]
 constexpr int kOffMisc = 256;                  // misc: int[4]
 constexpr int kOffApg = 512;                   // misc: int[kMaxR][npa]: A page ids of the tile
 constexpr int kMiscB = kOffApg + kMaxR * kMaxNpa * 4;
-constexpr int kVpB = kTileM * kVpRow * 2;
+constexpr int kVpB = kTileM * kMaxR * 2;      // packed V (uint16): hi or lo
 constexpr int kDsB = kTileM * kDsRow * 4;
 constexpr int kBufB = kStageB;
 static_assert(kVpB <= kBufB && kDsB <= kBufB, "expand buffers must fit the work buffers");
@@ -106,6 +105,13 @@ struct LdsBufs {
   char* b;
   char* c;
 };
+
+// Packed V (hi or lo parts, uint16): element (slot, k) sits at
+// ((k / 8) * kTileM + slot) * 8 + k % 8, k-group major, so the 16 lanes of an
+// MFMA operand read (16 slots, one 8-element k group) cover 256 contiguous
+// bytes; with slot-major rows the same read spreads over 16 rows and takes
+// twice the LDS cycles (bank conflicts).
+__device__ __forceinline__ int vp_index(int slot, int k) { return ((k >> 3) * kTileM + slot) * 8 + (k & 7); }
 
 // s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at
 // their maxima; vmcnt is split over bits 3:0 and 15:14).
@@ -461,24 +467,27 @@ __device__ __forceinline__ void load_v_tile(const float* v, int v_ld, const int*
                                             int rank, uint16_t* Vh, uint16_t* Vl) {
   constexpr int KW = 32 * NK;
   constexpr int PER = kTileM * KW / kMT;  // 8, 16, 24 or 32
+  static_assert(kTileM == 64, "packed V index: 64 slots x 8 elements per k group");
+  // thread element p is packed position p (vp_index order): slot (p / 8) % 64,
+  // k = 8 (p / 512) + p % 8
   for (int q0 = 0; q0 < PER; q0 += 8) {
     float f[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int idx = threadIdx.x + kMT * (q0 + q);
-      const int slot = idx / KW;
-      const int k = idx - slot * KW;
+      const int p = threadIdx.x + kMT * (q0 + q);
+      const int slot = (p >> 3) & (kTileM - 1);
+      const int k = ((p >> 9) << 3) | (p & 7);
       f[q] = v[(int64_t)toks[min(slot, count - 1)] * v_ld + min(k, rank - 1)];
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int idx = threadIdx.x + kMT * (q0 + q);
-      const int slot = idx / KW;
-      const int k = idx - slot * KW;
+      const int p = threadIdx.x + kMT * (q0 + q);
+      const int slot = (p >> 3) & (kTileM - 1);
+      const int k = ((p >> 9) << 3) | (p & 7);
       uint16_t hi, lo;
       MfmaOp<T>::split((slot < count && k < rank) ? f[q] : 0.f, hi, lo);
-      Vh[slot * kVpRow + k] = hi;
-      Vl[slot * kVpRow + k] = lo;
+      Vh[p] = hi;
+      Vl[p] = lo;
     }
   }
 }
@@ -550,11 +559,11 @@ __device__ __forceinline__ void expand_chunks(const PoolView& pv, const DevEntry
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       if (tb < ntb) {
-        const int vo = (16 * tb + r16) * kVpRow + 8 * g;
+        const int vo = vp_index(16 * tb + r16, 8 * g);  // + 4 k groups per k step
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
-          const uint4 vh = *reinterpret_cast<const uint4*>(Vh + vo + 32 * ks);
-          const uint4 vl = *reinterpret_cast<const uint4*>(Vl + vo + 32 * ks);
+          const uint4 vh = *reinterpret_cast<const uint4*>(Vh + vo + 32 * kTileM * ks);
+          const uint4 vl = *reinterpret_cast<const uint4*>(Vl + vo + 32 * kTileM * ks);
           const vec bk = as_vec<vec>(keep16m(bc[ks], kok[ks]));
           acc[tb] = MfmaOp<T>::mma(bk, as_vec<vec>(vh), acc[tb]);
           acc[tb] = MfmaOp<T>::mma(bk, as_vec<vec>(vl), acc[tb]);
@@ -672,14 +681,14 @@ __device__ __forceinline__ void expand_chunks_wide(const PoolView& pv, const Dev
     }
   };
   auto process = [&](int c, const uint4 (&bc)[JB][NK], const uint4 (&yc)[YP]) {
-    const int vo = r16 * kVpRow + 8 * g;
+    const int vo = vp_index(r16, 8 * g);  // + 4 k groups per k step
     f32x4_t acc[JB];
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      const uint4 vh = *reinterpret_cast<const uint4*>(Vh + vo + 32 * ks);
-      const uint4 vl = *reinterpret_cast<const uint4*>(Vl + vo + 32 * ks);
+      const uint4 vh = *reinterpret_cast<const uint4*>(Vh + vo + 32 * kTileM * ks);
+      const uint4 vl = *reinterpret_cast<const uint4*>(Vl + vo + 32 * kTileM * ks);
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
         const vec bk = as_vec<vec>(keep16m(bc[jb][ks], kok[ks]));
@@ -782,8 +791,8 @@ __device__ __forceinline__ void load_v_parts(const PlanView& pl, int c0, int c1,
         const float f = (sl < count && n + e < rank) ? a[e] : 0.f;
         uint16_t hi, lo;
         MfmaOp<T>::split(f, hi, lo);
-        Vh[sl * kVpRow + n + e] = hi;
-        Vl[sl * kVpRow + n + e] = lo;
+        Vh[vp_index(sl, n + e)] = hi;
+        Vl[vp_index(sl, n + e)] = lo;
       }
     }
   }
@@ -793,8 +802,8 @@ __device__ __forceinline__ void load_v_parts(const PlanView& pl, int c0, int c1,
   for (int idx = threadIdx.x; idx < 16 * ntb * (KW - w0); idx += kMT) {
     const int sl = idx / (KW - w0);
     const int k = w0 + idx - sl * (KW - w0);
-    Vh[sl * kVpRow + k] = 0;
-    Vl[sl * kVpRow + k] = 0;
+    Vh[vp_index(sl, k)] = 0;
+    Vl[vp_index(sl, k)] = 0;
   }
 }
 
