@@ -153,11 +153,16 @@ def main():
     n = len(batches[0].ids)
     v = [torch.zeros((n, sp.max_rank), dtype=torch.float32, device="cuda") for _ in slices]
     plans = []
+    plan_host = {}
     if planned:
+        t_build = []
         for b in batches:
             p = L.lora_plan_create(sp.handle, len(b.ids))
+            t = time.perf_counter()
             L.lora_plan_build(p, b.ids, args.l_long)
+            t_build.append(time.perf_counter() - t)
             plans.append(p)
+        plan_host["plan_build_us"] = float(np.median(t_build)) * 1e6
     stream = torch.cuda.current_stream()
 
     def step(i):
@@ -177,6 +182,21 @@ def main():
                 L.lora_bgmv_shrink(sp.handle, s, xs[k][j], ids_d[k], v[j], stream=stream)
                 L.lora_bgmv_expand(sp.handle, s, v[j], ids_d[k], ys[k][j], ydt, stream=stream)
 
+    if planned:
+        # host time of a plan's first launch (it builds the block ranges of the
+        # launch shape) and of a later launch (ranges cached); untimed
+        t_first, t_cached = [], []
+        for k in range(len(batches)):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            step(k)
+            t_first.append(time.perf_counter() - t)
+            t = time.perf_counter()
+            step(k)
+            t_cached.append(time.perf_counter() - t)
+        torch.cuda.synchronize()
+        plan_host["first_launch_host_us"] = float(np.median(t_first)) * 1e6
+        plan_host["cached_launch_host_us"] = float(np.median(t_cached)) * 1e6
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -237,6 +257,8 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
         "accumulate": "f32",
     }
+    if plan_host:
+        out["plan_host_us"] = plan_host  # median per batch; host wall clock, outside the timed region
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(wl, batches, slices, threads)
