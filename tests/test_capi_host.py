@@ -31,6 +31,13 @@ def test_library_exports_every_declared_symbol():
         assert getattr(L.lib(), s) is not None
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no fallback path: without the built library the binding refuses to load
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "liblora_mi355x.so"))
+    with pytest.raises(ImportError, match="not built"):
+        L._load()
+
+
 def test_library_has_gfx950_code_object():
     # the offload bundle of the library built here names its target
     with open(L.LIB_PATH, "rb") as f:
