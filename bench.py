@@ -1,6 +1,6 @@
 """Throughput of the heterogeneous-adapter LoRA apply on one MI355X.
 
-Default workload: Llama-7B decode BGMV -- 64 tokens (one per request), the
+Headline workload: Llama-7B decode BGMV -- 64 tokens (one per request), the
 q/k/v/o projections (4096 -> 4096) of one layer, 1000 rank-16 fp16 adapters
 scattered over a unified page pool.  A step applies every token's adapter to
 all four projections: y_i += s_a B_a (A_a x_i), shrink and expand fused in one
@@ -8,16 +8,20 @@ launch (lora_bgmv_apply).  16 different id batches (with their own x and y
 buffers) rotate, so adapter pages come from HBM rather than the 256 MB
 Infinity Cache.
 
-`--workload` runs one of the other synthetic workloads the same way (for
-profiling; the default is the measured configuration): the heterogeneous
-decode batch (lora_bgmv_apply over its two slices) or a planned batch
-(lora_apply over all slices; plans are built before the timed region).
+The same run then times the other workloads of the metric (unless
+--no-extra), each under `workloads` in the JSON line with its own algorithmic
+bytes and roofline fraction: the heterogeneous decode batch through
+lora_bgmv_apply and through a host plan (lora_apply), the Llama-13B prefill
+SGMV batch and the Llama-70B-shape mixed batch (lora_apply on MFMA tiles), plus
+a plain device copy and a streaming read as the measured bandwidth ceiling.
 
+`--workload` makes another workload the headline (for profiling runs).
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +34,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "BGMV/SGMV tokens/s and achieved HBM GB/s (% of peak), Llama-7B/70B shapes, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+WORKLOADS = {"llama7b_decode_bgmv": 1, "hetero_decode_bgmv": 2, "llama13b_prefill_sgmv": 3,
+             "llama70b_mixed_apply": 4}
+CSRC = os.path.join(ROOT, "gather_lora_matmul_amd", "csrc")
+# Sources each path's kernels are compiled from (traffic figures taken on other
+# code are dropped).
+BGMV_SOURCES = ("k_bgmv.hip", "kcommon.h", "kvalu.h", "lora_internal.h")
+PLANNED_SOURCES = ("k_sgmv.hip", "kmfma.h", "kcommon.h", "kvalu.h", "lora_internal.h",
+                   "layout.cpp", "plan.cpp")
 
 
 def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int) -> int:
@@ -47,60 +59,229 @@ def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int) -> int:
     return total
 
 
-# The sources the decode kernel (k_bgmv_apply) is compiled from.
-DECODE_SOURCES = ("k_bgmv.hip", "kcommon.h", "kvalu.h", "lora_internal.h")
-
-
-def kernel_source_hash() -> str:
-    """Hash of the decode kernel's sources, so counter figures taken on other
-    code are dropped."""
-    import hashlib
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gather_lora_matmul_amd", "csrc")
-    paths = [os.path.join(csrc, f) for f in DECODE_SOURCES]
-    paths.append(os.path.join(ROOT, "include", "lora_mi355x.h"))
+    paths = [os.path.join(CSRC, f) for f in files] + [os.path.join(ROOT, "include", "lora_mi355x.h")]
     for path in paths:
         with open(path, "rb") as fh:
             h.update(os.path.basename(path).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the fused decode kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None if the kernel sources
-    changed since the counters were taken."""
-    prof = os.path.join(ROOT, "profiles", "bgmv_apply_llama7b_decode_traffic.json")
+def measured_traffic(workload: str, entry: str, src_hash: str):
+    """HBM bytes per step of `entry` on `workload` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (profiles/hbm_traffic.json), or None if
+    there is none or the kernels' sources changed since it was taken."""
     try:
-        with open(prof) as f:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
             tj = json.load(f)
     except (OSError, ValueError):
         return None
-    if tj.get("kernel_source_hash") != kernel_source_hash():
+    rec = tj.get("records", {}).get("%s/%s" % (workload, entry))
+    if not rec or rec.get("kernel_source_hash") != src_hash:
         return None
-    return tj.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_step")
 
 
-def cpu_baseline(wl, batches, slices, threads: int, min_s: float = 10.0):
-    """The fp64 oracle on the host, over whole batches of the same workload,
-    repeated until at least `min_s` seconds of CPU work have been timed."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_rate(wl, batches, slices, threads: int, min_s: float):
+    """Tokens/s of the fp64 oracle over whole batches of the workload, repeated
+    until at least `min_s` seconds of CPU work have been timed."""
     import oracle
     t0 = time.perf_counter()
-    ntok = 0
-    calls = 0
-    while True:
-        for b in batches:
-            for s in slices:
-                oracle.workload_reference(wl, b, s, n_threads=threads)
-            ntok += len(b.ids)
-            calls += 1
-            if time.perf_counter() - t0 >= min_s:
-                break
-        if time.perf_counter() - t0 >= min_s:
-            break
+    ntok = calls = 0
+    while time.perf_counter() - t0 < min_s:
+        b = batches[calls % len(batches)]
+        for s in slices:
+            oracle.workload_reference(wl, b, s, n_threads=threads)
+        ntok += len(b.ids)
+        calls += 1
     dt = time.perf_counter() - t0
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d batches of this workload (%d distinct) x %d slices = %d tokens, "
-                      "fp64 C oracle, %.1f s" % (calls, len(batches), len(slices), ntok, dt)}
+    return ntok / dt, calls, ntok, dt
+
+
+def cpu_baseline(wl, batches, slices):
+    """The oracle as it stands on the host: all the threads this process may use
+    (at most 16, the machine's CPU share for one GPU) and one thread."""
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count() or 1
+    threads = max(1, min(16, allowed))
+    rate, calls, ntok, dt = oracle_rate(wl, batches, slices, threads, 10.0)
+    rate1, calls1, ntok1, dt1 = oracle_rate(wl, batches, slices, 1, 5.0)
+    return {"value": rate, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d batches of this workload (%d distinct) x %d slices = %d tokens, fp64 C "
+                      "oracle, %.1f s on %d threads" % (calls, len(batches), len(slices), ntok, dt,
+                                                        threads),
+            "value_1_thread": rate1,
+            "sample_1_thread": "%d batches = %d tokens, %.1f s" % (calls1, ntok1, dt1),
+            "host_cpus": os.cpu_count(), "affinity_cpus": allowed, "cpu_model": cpu_model()}
+
+
+class Runner:
+    """One workload set up for timing: pool, rotating batches, plans and
+    workspaces, and the step that applies one batch."""
+
+    def __init__(self, name: str, mode: str = "fused", planned: bool = False, n_batches=None,
+                 l_long: int = 0):
+        import torch
+
+        import gather_lora_matmul_amd as L
+        import workloads as W
+        from gather_lora_matmul_amd.synthetic import SyntheticPool, prepare_shapes, to_device
+        self.L, self.torch = L, torch
+        cfg = WORKLOADS[name]
+        self.wl = wl = W.make_workload(cfg)
+        self.planned = planned or cfg >= 3
+        self.mode = mode
+        self.slices = slices = list(range(len(wl.slices)))
+        n_batches = n_batches or (4 if self.planned else 16)
+        t0 = time.perf_counter()
+        print("[bench] %s: pool of %d adapters x %d slices" % (name, wl.n_adapters, len(slices)),
+              file=sys.stderr, flush=True)
+        self.sp = SyntheticPool(wl)
+        self.setup_s = time.perf_counter() - t0
+        self.batches = [W.make_batch(wl, i) for i in range(n_batches)]
+        self.ids_d = [torch.from_numpy(b.ids).cuda() for b in self.batches]
+        self.xs = [[to_device(b.x[s], wl.dtype) for s in slices] for b in self.batches]
+        self.ys = [[to_device(b.y0[s], wl.dtype) for s in slices] for b in self.batches]
+        self.ydt = W.DTYPE_CODE[wl.dtype]
+        self.n = len(self.batches[0].ids)
+        self.v = [torch.zeros((self.n, self.sp.max_rank), dtype=torch.float32, device="cuda")
+                  for _ in slices]
+        self.plans, self.wss, self.plan_host = [], [], {}
+        if self.planned:
+            t_build, t_prep = [], []
+            shapes = [slices] if mode == "fused" else [[s] for s in slices]
+            for b in self.batches:
+                p = L.lora_plan_create(self.sp.handle, len(b.ids))
+                t = time.perf_counter()
+                L.lora_plan_build(p, b.ids, l_long)
+                t_build.append(time.perf_counter() - t)
+                t = time.perf_counter()
+                self.wss.append(prepare_shapes(p, shapes))
+                t_prep.append(time.perf_counter() - t)
+                self.plans.append(p)
+            torch.cuda.synchronize()
+            self.plan_host["plan_build_us"] = float(np.median(t_build)) * 1e6
+            self.plan_host["prepare_us"] = float(np.median(t_prep)) * 1e6
+        self.stream = torch.cuda.current_stream()
+        self.entry = (("lora_apply" if self.planned else "lora_bgmv_apply") if mode == "fused"
+                      else ("lora_sgmv_shrink+expand" if self.planned else "lora_bgmv_shrink+expand"))
+        self.src_hash = source_hash(PLANNED_SOURCES if self.planned else BGMV_SOURCES)
+
+    def step(self, i: int):
+        L, k = self.L, i % len(self.batches)
+        io = [(s, self.xs[k][j], self.ys[k][j]) for j, s in enumerate(self.slices)]
+        if self.planned:
+            if self.mode == "fused":
+                L.lora_apply(self.sp.handle, self.plans[k], io, self.ydt, workspace=self.wss[k],
+                             stream=self.stream)
+            else:
+                for j, s in enumerate(self.slices):
+                    L.lora_sgmv_shrink(self.sp.handle, self.plans[k], s, self.xs[k][j], self.v[j],
+                                       workspace=self.wss[k], stream=self.stream)
+                    L.lora_sgmv_expand(self.sp.handle, self.plans[k], s, self.v[j],
+                                       self.ys[k][j], self.ydt, stream=self.stream)
+        elif self.mode == "fused":
+            L.lora_bgmv_apply(self.sp.handle, io, self.ids_d[k], self.ydt, stream=self.stream)
+        else:
+            for j, s in enumerate(self.slices):
+                L.lora_bgmv_shrink(self.sp.handle, s, self.xs[k][j], self.ids_d[k], self.v[j],
+                                   stream=self.stream)
+                L.lora_bgmv_expand(self.sp.handle, s, self.v[j], self.ids_d[k], self.ys[k][j],
+                                   self.ydt, stream=self.stream)
+
+    def time(self, steps: int, warmup: int):
+        """Wall clock over exactly `steps` steps, bracketed by HIP events on the
+        stream the kernels are launched on."""
+        torch = self.torch
+        if self.planned:  # host time of one planned step (checks and launches), untimed
+            t_launch = []
+            for k in range(len(self.batches)):
+                torch.cuda.synchronize()
+                t = time.perf_counter()
+                self.step(k)
+                t_launch.append(time.perf_counter() - t)
+            self.plan_host["launch_host_us"] = float(np.median(t_launch)) * 1e6
+        for i in range(warmup):
+            self.step(i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(self.stream)
+        for i in range(steps):
+            self.step(warmup + i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        event_s = e0.elapsed_time(e1) * 1e-3 / steps
+        used = [algorithmic_bytes(self.wl, self.batches[(warmup + i) % len(self.batches)].ids,
+                                  self.slices, 2) for i in range(steps)]
+        return wall, event_s, float(np.mean(used))
+
+    def record(self, steps: int, warmup: int):
+        wall, event_s, avg_bytes = self.time(steps, warmup)
+        achieved = avg_bytes / event_s / 1e9
+        rec = {"entry": self.entry, "tokens_per_step": self.n, "steps": steps, "warmup": warmup,
+               "tokens_per_s": self.n * steps / wall, "ms_per_step": wall * 1e3 / steps,
+               "event_us_per_step": event_s * 1e6, "algorithmic_MB_per_step": avg_bytes / 1e6,
+               "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                            "basis": "algorithmic bytes / (HIP-event time of the timed steps / "
+                                     "steps), launch gaps included",
+                            "traffic": measured_traffic(self.wl.name, self.entry, self.src_hash)},
+               "kernel_source_hash": self.src_hash, "pool_setup_s": self.setup_s}
+        if self.plan_host:
+            rec["plan_host_us"] = self.plan_host
+        return rec
+
+    def close(self):
+        for p in self.plans:
+            self.L.lora_plan_destroy(p)
+        self.plans = []
+        self.sp.close()
+
+
+def bandwidth_ceiling():
+    """Measured device bandwidth of plain streaming kernels on 1 GiB buffers
+    (beyond the 256 MB Infinity Cache): a device-to-device copy (read + write
+    bytes) and a sum (read bytes)."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+        src.sum()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    for _ in range(10):
+        dst.copy_(src)
+    e[1].record()
+    e[2].record()
+    for _ in range(10):
+        src.sum()
+    e[3].record()
+    torch.cuda.synchronize()
+    copy_s = e[0].elapsed_time(e[1]) * 1e-3 / 10
+    read_s = e[2].elapsed_time(e[3]) * 1e-3 / 10
+    del src, dst
+    return {"copy_GBs": 2 * 4 * n / copy_s / 1e9, "read_GBs": 4 * n / read_s / 1e9,
+            "bytes": 4 * n, "kernels": "torch copy_ and sum over 1 GiB fp32, 10 calls each"}
 
 
 def main():
@@ -109,9 +290,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=["fused", "split"], default="fused")
-    ap.add_argument("--workload", default="llama7b_decode_bgmv",
-                    choices=["llama7b_decode_bgmv", "hetero_decode_bgmv", "llama13b_prefill_sgmv",
-                             "llama70b_mixed_apply"])
+    ap.add_argument("--workload", default="llama7b_decode_bgmv", choices=sorted(WORKLOADS))
     ap.add_argument("--batches", type=int, default=None,
                     help="rotating batches (default 16 for decode, 4 for planned batches)")
     ap.add_argument("--planned", action="store_true",
@@ -121,6 +300,8 @@ def main():
                     help="planned batches: groups shorter than this run as short VALU items "
                          "(0: every group of a 16-bit pool is an MFMA tile)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the headline workload")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 64 MiB device copy 10x (HBM counter calibration)")
     args = ap.parse_args()
@@ -130,141 +311,64 @@ def main():
         sys.exit(2)
 
     import torch
-
-    import gather_lora_matmul_amd as L
-    import workloads as W
-    from gather_lora_matmul_amd.synthetic import SyntheticPool, to_device
-
     torch.cuda.set_device(0)
-    cfg = {"llama7b_decode_bgmv": 1, "hetero_decode_bgmv": 2, "llama13b_prefill_sgmv": 3,
-           "llama70b_mixed_apply": 4}[args.workload]
-    wl = W.make_workload(cfg)
-    planned = cfg >= 3 or args.planned
-    slices = list(range(len(wl.slices)))
-    n_batches = args.batches or (4 if planned else 16)
-    print("[bench] building pool: %s, %d adapters x %d slices" % (wl.name, wl.n_adapters, len(slices)),
-          file=sys.stderr, flush=True)
-    sp = SyntheticPool(wl)
-    batches = [W.make_batch(wl, i) for i in range(n_batches)]
-    ids_d = [torch.from_numpy(b.ids).cuda() for b in batches]
-    xs = [[to_device(b.x[s], wl.dtype) for s in slices] for b in batches]
-    ys = [[to_device(b.y0[s], wl.dtype) for s in slices] for b in batches]
-    ydt = W.DTYPE_CODE[wl.dtype]
-    n = len(batches[0].ids)
-    v = [torch.zeros((n, sp.max_rank), dtype=torch.float32, device="cuda") for _ in slices]
-    plans = []
-    plan_host = {}
-    if planned:
-        t_build = []
-        for b in batches:
-            p = L.lora_plan_create(sp.handle, len(b.ids))
-            t = time.perf_counter()
-            L.lora_plan_build(p, b.ids, args.l_long)
-            t_build.append(time.perf_counter() - t)
-            plans.append(p)
-        plan_host["plan_build_us"] = float(np.median(t_build)) * 1e6
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        k = i % len(batches)
-        io = [(s, xs[k][j], ys[k][j]) for j, s in enumerate(slices)]
-        if planned:
-            if args.mode == "fused":
-                L.lora_apply(sp.handle, plans[k], io, ydt, stream=stream)
-            else:
-                for j, s in enumerate(slices):
-                    L.lora_sgmv_shrink(sp.handle, plans[k], s, xs[k][j], v[j], stream=stream)
-                    L.lora_sgmv_expand(sp.handle, plans[k], s, v[j], ys[k][j], ydt, stream=stream)
-        elif args.mode == "fused":
-            L.lora_bgmv_apply(sp.handle, io, ids_d[k], ydt, stream=stream)
-        else:
-            for j, s in enumerate(slices):
-                L.lora_bgmv_shrink(sp.handle, s, xs[k][j], ids_d[k], v[j], stream=stream)
-                L.lora_bgmv_expand(sp.handle, s, v[j], ids_d[k], ys[k][j], ydt, stream=stream)
-
-    if planned:
-        # host time of a plan's first launch (it builds the block ranges of the
-        # launch shape) and of a later launch (ranges cached); untimed
-        t_first, t_cached = [], []
-        for k in range(len(batches)):
-            torch.cuda.synchronize()
-            t = time.perf_counter()
-            step(k)
-            t_first.append(time.perf_counter() - t)
-            t = time.perf_counter()
-            step(k)
-            t_cached.append(time.perf_counter() - t)
-        torch.cuda.synchronize()
-        plan_host["first_launch_host_us"] = float(np.median(t_first)) * 1e6
-        plan_host["cached_launch_host_us"] = float(np.median(t_cached)) * 1e6
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # timed region: wall clock over exactly K steps, bracketed by HIP events on
-    # the stream the kernels are launched on (average launch duration =
-    # event time / K; one launch per step in the fused mode)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = np.array([e0.elapsed_time(e1) / args.steps])
-    ms_per_step = wall * 1e3 / args.steps
-    toks = n * args.steps / wall
-    elt_y = 2
-    step_bytes = [algorithmic_bytes(wl, b.ids, slices, elt_y) for b in batches]
-    used = [step_bytes[(args.warmup + i) % len(batches)] for i in range(args.steps)]
-    avg_bytes = float(np.mean(used))
-    avg_kernel_s = float(np.mean(kern_ms)) * 1e-3
-    achieved = avg_bytes / avg_kernel_s / 1e9
-    traffic = measured_traffic() if args.mode == "fused" and cfg == 1 and not planned else None
+    head = Runner(args.workload, args.mode, args.planned, args.batches, args.l_long)
+    rec = head.record(args.steps, args.warmup)
+    wl = head.wl
+    cfg = WORKLOADS[args.workload]
+    out = {
+        "metric": METRIC,
+        "value": rec["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens_per_step": head.n,
+                   "slices": ", ".join("%dx%d" % tuple(d) for d in wl.slices),
+                   "adapters": wl.n_adapters,
+                   "rank": sorted(set(int(r) for r in wl.ranks)) if cfg != 1 else 16,
+                   "weights": "%s N(0,0.02), pages scattered" % wl.dtype,
+                   "entry": head.entry, "id_batches_rotated": len(head.batches)},
+        "roofline": rec["roofline"],
+        "kernel_us_per_step": rec["event_us_per_step"],
+        "algorithmic_MB_per_step": rec["algorithmic_MB_per_step"],
+        "kernel_source_hash": rec["kernel_source_hash"],
+        "accumulate": "f32",
+    }
+    if "plan_host_us" in rec:
+        out["plan_host_us"] = rec["plan_host_us"]
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, head.batches, head.slices)
     if args.copy_calib:
         src = torch.empty(64 << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(10):
             dst.copy_(src)
         torch.cuda.synchronize()
-    out = {
-        "metric": METRIC,
-        "value": toks,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic",
-        "config": {"workload": wl.name, "tokens_per_step": n,
-                   "slices": ", ".join("%dx%d" % tuple(d) for d in wl.slices),
-                   "adapters": wl.n_adapters,
-                   "rank": sorted(set(int(r) for r in wl.ranks)) if cfg != 1 else 16,
-                   "weights": "%s N(0,0.02), pages scattered" % wl.dtype,
-                   "entry": ("lora_apply" if planned else "lora_bgmv_apply") if args.mode == "fused"
-                   else ("lora_sgmv_shrink+expand" if planned else "lora_bgmv_shrink+expand"),
-                   "id_batches_rotated": len(batches)},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
-        "kernel_us_per_step": float(np.mean(kern_ms)) * 1e3,
-        "algorithmic_MB_per_step": avg_bytes / 1e6,
-        "kernel_source_hash": kernel_source_hash(),
-        "accumulate": "f32",
-    }
-    if plan_host:
-        out["plan_host_us"] = plan_host  # median per batch; host wall clock, outside the timed region
-    if not args.no_cpu:
-        threads = min(16, os.cpu_count() or 1)
-        out["cpu_baseline"] = cpu_baseline(wl, batches, slices, threads)
-    for p in plans:
-        L.lora_plan_destroy(p)
-    sp.close()
+    head.close()
+    if not args.no_extra:
+        extra = {}
+        steps = min(args.steps, 50)
+        warm = min(args.warmup, 5)
+        for name, planned in (("hetero_decode_bgmv", False), ("hetero_decode_bgmv", True),
+                              ("llama13b_prefill_sgmv", True), ("llama70b_mixed_apply", True)):
+            key = name + ("/planned" if planned and WORKLOADS[name] < 3 else "")
+            if name == args.workload and planned == head.planned:
+                continue
+            r = Runner(name, "fused", planned)
+            extra[key] = r.record(steps, warm)
+            r.close()
+            print("[bench] %s: %.1f us per step, %.3f of 8 TB/s" % (
+                key, extra[key]["event_us_per_step"], extra[key]["roofline"]["frac"]),
+                file=sys.stderr, flush=True)
+        out["workloads"] = extra
+        out["bandwidth_ceiling"] = bandwidth_ceiling()
     print(json.dumps(out), flush=True)
 
 

@@ -34,8 +34,9 @@ EXPORTS = (
     "lora_pool_free_pages", "lora_pool_upload", "lora_pool_evict", "lora_page_table_build",
     "lora_pool_export_entry", "lora_pool_read_pages", "lora_bgmv_shrink", "lora_bgmv_expand",
     "lora_bgmv_apply", "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
-    "lora_plan_get_stats", "lora_plan_export", "lora_sgmv_shrink", "lora_sgmv_expand",
-    "lora_apply", "lora_debug_resolve", "lora_debug_gather", "lora_last_error",
+    "lora_plan_get_stats", "lora_plan_export", "lora_plan_prepare", "lora_workspace_size",
+    "lora_sgmv_shrink", "lora_sgmv_expand", "lora_apply", "lora_debug_resolve",
+    "lora_debug_gather", "lora_last_error",
 )
 
 
@@ -98,9 +99,11 @@ def _load() -> ctypes.CDLL:
         "lora_plan_build": [V, V, I32, I32, V],
         "lora_plan_get_stats": [V, ctypes.POINTER(PlanStats)],
         "lora_plan_export": [V, V, V],
-        "lora_sgmv_shrink": [V, V, I32, V, V, I32, V],
+        "lora_plan_prepare": [V, I32, ctypes.POINTER(Io), V],
+        "lora_workspace_size": [V, I32, ctypes.POINTER(Io), ctypes.POINTER(ctypes.c_size_t)],
+        "lora_sgmv_shrink": [V, V, I32, V, V, I32, V, ctypes.c_size_t, V],
         "lora_sgmv_expand": [V, V, I32, V, I32, V, I32, V],
-        "lora_apply": [V, V, I32, ctypes.POINTER(Io), I32, V],
+        "lora_apply": [V, V, I32, ctypes.POINTER(Io), I32, V, ctypes.c_size_t, V],
         "lora_debug_resolve": [V, I32, V, I32, V, V, V],
         "lora_debug_gather": [V, I32, I32, V, V, V],
     }
@@ -141,6 +144,47 @@ def _dev_ptr(t) -> int:
     return t.data_ptr()
 
 
+# Shapes of the pools created through this binding (handle -> (dtype, slice
+# dims, max_rank)), so that buffers can be checked before a call: the C ABI
+# takes raw pointers and cannot see their sizes or element types.
+_POOLS = {}
+_PLAN_POOL = {}
+_DT_NAME = {0: "float32", 1: "float16", 2: "bfloat16"}
+
+
+def _check_tensor(t, what: str, dtype_code: Optional[int], min_numel: int):
+    import torch
+    if t is None:
+        raise ValueError("%s: missing tensor" % what)
+    if dtype_code is not None and t.dtype != getattr(torch, _DT_NAME[dtype_code]):
+        raise TypeError("%s: dtype %s, expected %s" % (what, t.dtype, _DT_NAME[dtype_code]))
+    if t.numel() < min_numel:
+        raise ValueError("%s: %d elements, the call reads or writes %d" % (what, t.numel(), min_numel))
+
+
+def _check_ids(ids):
+    import torch
+    if ids.dtype != torch.int32 or ids.dim() != 1:
+        raise TypeError("ids: expected a 1-D int32 tensor, got %s %s" % (ids.dtype, tuple(ids.shape)))
+
+
+def _check_io(pool: int, ios, n: int, y_dtype: int):
+    info = _POOLS.get(pool)
+    for k, (s, x, y) in enumerate(ios):
+        if info is None:
+            continue
+        dt, dims, _ = info
+        if not 0 <= int(s) < len(dims):
+            continue  # the library reports the bad slice
+        d_in, d_out = dims[int(s)]
+        _check_tensor(x, "io %d x" % k, dt, n * d_in)
+        _check_tensor(y, "io %d y" % k, y_dtype, n * d_out)
+
+
+def _check_v(pool: int, v, n: int, v_ld: int):
+    _check_tensor(v, "v", 0, n * v_ld)
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -165,10 +209,12 @@ def lora_pool_create(page_elems: int, dtype: int, n_pages: int, max_adapters: in
                  shuffle_seed, flags, _dev_ptr(pages_dev) if pages_dev is not None else None)
     h = ctypes.c_void_p()
     _check(_lib.lora_pool_create(ctypes.byref(d), ctypes.byref(h)), "lora_pool_create")
+    _POOLS[h.value] = (int(dtype), [(int(a), int(b)) for a, b in slice_dims], int(max_rank))
     return h.value
 
 
 def lora_pool_destroy(pool: int):
+    _POOLS.pop(pool, None)
     _check(_lib.lora_pool_destroy(pool), "lora_pool_destroy")
 
 
@@ -236,16 +282,28 @@ def lora_pool_read_pages(pool: int, first: int, count: int, page_elems: int, dty
 # BGMV
 # ----------------------------------------------------------------------------
 def lora_bgmv_shrink(pool: int, slice_: int, x, ids, v, v_ld: Optional[int] = None, stream=None):
+    _check_ids(ids)
     n = int(ids.shape[0])
     v_ld = int(v.shape[1]) if v_ld is None else v_ld
+    info = _POOLS.get(pool)
+    if info is not None and 0 <= slice_ < len(info[1]):
+        _check_tensor(x, "x", info[0], n * info[1][slice_][0])
+    _check_v(pool, v, n, v_ld)
     _check(_lib.lora_bgmv_shrink(pool, slice_, _dev_ptr(x), _dev_ptr(ids), n, _dev_ptr(v), v_ld,
                                  _stream(stream)), "lora_bgmv_shrink")
 
 
 def lora_bgmv_expand(pool: int, slice_: int, v, ids, y, y_dtype: int, token_scale=None,
                      v_ld: Optional[int] = None, stream=None):
+    _check_ids(ids)
     n = int(ids.shape[0])
     v_ld = int(v.shape[1]) if v_ld is None else v_ld
+    info = _POOLS.get(pool)
+    if info is not None and 0 <= slice_ < len(info[1]):
+        _check_tensor(y, "y", y_dtype, n * info[1][slice_][1])
+    _check_v(pool, v, n, v_ld)
+    if token_scale is not None:
+        _check_tensor(token_scale, "token_scale", 0, n)
     _check(_lib.lora_bgmv_expand(pool, slice_, _dev_ptr(v), v_ld, _dev_ptr(ids), n,
                                  _dev_ptr(token_scale), _dev_ptr(y), y_dtype, _stream(stream)),
            "lora_bgmv_expand")
@@ -261,6 +319,8 @@ def _ios(ios: Sequence[Tuple[int, object, object]]):
 def lora_bgmv_apply(pool: int, ios: Sequence[Tuple[int, object, object]], ids, y_dtype: int,
                     stream=None):
     """ios: [(slice, x, y), ...] sharing `ids`."""
+    _check_ids(ids)
+    _check_io(pool, ios, int(ids.shape[0]), y_dtype)
     arr = _ios(ios)
     _check(_lib.lora_bgmv_apply(pool, len(ios), arr, _dev_ptr(ids), int(ids.shape[0]), y_dtype,
                                 _stream(stream)), "lora_bgmv_apply")
@@ -272,10 +332,12 @@ def lora_bgmv_apply(pool: int, ios: Sequence[Tuple[int, object, object]], ids, y
 def lora_plan_create(pool: int, max_tokens: int) -> int:
     h = ctypes.c_void_p()
     _check(_lib.lora_plan_create(pool, max_tokens, ctypes.byref(h)), "lora_plan_create")
+    _PLAN_POOL[h.value] = pool
     return h.value
 
 
 def lora_plan_destroy(plan: int):
+    _PLAN_POOL.pop(plan, None)
     _check(_lib.lora_plan_destroy(plan), "lora_plan_destroy")
 
 
@@ -306,24 +368,70 @@ def lora_plan_export(plan: int) -> Tuple[np.ndarray, np.ndarray]:
     return perm, items
 
 
+def _slice_ios(slices: Sequence[int]):
+    arr = (Io * len(slices))()
+    for k, s in enumerate(slices):
+        arr[k] = Io(int(s), 0, None, None)
+    return arr
+
+
+def lora_plan_prepare(plan: int, slices: Sequence[int], stream=None):
+    """Prepare the launch shape `slices` (the slices of a planned call, in order)."""
+    arr = _slice_ios(slices)
+    _check(_lib.lora_plan_prepare(plan, len(slices), arr, _stream(stream)), "lora_plan_prepare")
+
+
+def lora_workspace_size(plan: int, slices: Sequence[int]) -> int:
+    arr = _slice_ios(slices)
+    out = ctypes.c_size_t()
+    _check(_lib.lora_workspace_size(plan, len(slices), arr, ctypes.byref(out)),
+           "lora_workspace_size")
+    return int(out.value)
+
+
+def _ws(workspace):
+    """(pointer, bytes) of a caller-owned device workspace tensor (or None)."""
+    if workspace is None:
+        return None, 0
+    return _dev_ptr(workspace), int(workspace.numel() * workspace.element_size())
+
+
+def _plan_tokens(plan: int) -> int:
+    return lora_plan_get_stats(plan)["n_tokens"]
+
+
 def lora_sgmv_shrink(pool: int, plan: int, slice_: int, x, v, v_ld: Optional[int] = None,
-                     stream=None):
+                     workspace=None, stream=None):
     v_ld = int(v.shape[1]) if v_ld is None else v_ld
-    _check(_lib.lora_sgmv_shrink(pool, plan, slice_, _dev_ptr(x), _dev_ptr(v), v_ld,
+    n = _plan_tokens(plan)
+    info = _POOLS.get(pool)
+    if info is not None and 0 <= slice_ < len(info[1]):
+        _check_tensor(x, "x", info[0], n * info[1][slice_][0])
+    _check_v(pool, v, n, v_ld)
+    wp, wb = _ws(workspace)
+    _check(_lib.lora_sgmv_shrink(pool, plan, slice_, _dev_ptr(x), _dev_ptr(v), v_ld, wp, wb,
                                  _stream(stream)), "lora_sgmv_shrink")
 
 
 def lora_sgmv_expand(pool: int, plan: int, slice_: int, v, y, y_dtype: int,
                      v_ld: Optional[int] = None, stream=None):
     v_ld = int(v.shape[1]) if v_ld is None else v_ld
+    n = _plan_tokens(plan)
+    info = _POOLS.get(pool)
+    if info is not None and 0 <= slice_ < len(info[1]):
+        _check_tensor(y, "y", y_dtype, n * info[1][slice_][1])
+    _check_v(pool, v, n, v_ld)
     _check(_lib.lora_sgmv_expand(pool, plan, slice_, _dev_ptr(v), v_ld, _dev_ptr(y), y_dtype,
                                  _stream(stream)), "lora_sgmv_expand")
 
 
 def lora_apply(pool: int, plan: int, ios: Sequence[Tuple[int, object, object]], y_dtype: int,
-               stream=None):
+               workspace=None, stream=None):
+    _check_io(pool, ios, _plan_tokens(plan), y_dtype)
     arr = _ios(ios)
-    _check(_lib.lora_apply(pool, plan, len(ios), arr, y_dtype, _stream(stream)), "lora_apply")
+    wp, wb = _ws(workspace)
+    _check(_lib.lora_apply(pool, plan, len(ios), arr, y_dtype, wp, wb, _stream(stream)),
+           "lora_apply")
 
 
 # ----------------------------------------------------------------------------

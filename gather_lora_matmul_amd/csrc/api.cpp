@@ -1,6 +1,8 @@
-// Compute entry points of the C ABI: argument and state checks, then one
-// stream-ordered launch (or two, for plans that mix MFMA tiles and short
-// items in the split API).  Nothing here blocks the host.
+// Compute entry points of the C ABI: argument and state checks, then
+// stream-ordered launches.  Nothing here allocates memory or waits for the
+// device: planned calls find their launch shape's layout among those the plan
+// prepared (lora_plan_prepare) and take the partial-tile workspace from the
+// caller.
 #include <algorithm>
 #include <cstring>
 
@@ -71,6 +73,25 @@ IoSet single_io(const IoDesc& io) {
   return s;
 }
 
+// The prepared layout of a planned call's launch shape and the check of the
+// caller's workspace against it (none needed without MFMA tiles).
+lora_status find_layout(const lora_plan* pl, const IoSet& ios, const void* ws, size_t ws_bytes,
+                        bool needs_ws, const PlanLayout** out) {
+  *out = nullptr;
+  if (pl->n_mfma == 0) return LORA_OK;
+  const PlanLayout* lay = plan_find_layout(pl, ios);
+  if (!lay) return fail(LORA_E_STATE, "launch shape not prepared: call lora_plan_prepare after lora_plan_build");
+  if (needs_ws) {
+    const size_t need = 16 * (size_t)lay->part_units;
+    if (ws_bytes < need || (need && !ws))
+      return fail(LORA_E_ARG, "workspace of %zu bytes, this launch needs %zu (lora_workspace_size)",
+                  ws_bytes, need);
+    if ((uintptr_t)ws & 15u) return fail(LORA_E_ARG, "workspace not 16-byte aligned");
+  }
+  *out = lay;
+  return LORA_OK;
+}
+
 }  // namespace
 
 #define LORA_TRY(expr)          \
@@ -128,9 +149,9 @@ lora_status lora_bgmv_apply(lora_pool* p, int32_t n_io, const lora_io* io, const
 }
 
 lora_status lora_sgmv_shrink(lora_pool* p, const lora_plan* pl, int32_t slice, const void* x,
-                             float* v, int32_t v_ld, void* stream) {
+                             float* v, int32_t v_ld, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  LORA_TRY(check_pool(p));
+  if (!p) return fail(LORA_E_ARG, "null pool");
   LORA_TRY(check_plan(p, pl));
   LORA_TRY(check_slice(p, slice));
   if (pl->n_tokens == 0) return LORA_OK;
@@ -139,8 +160,10 @@ lora_status lora_sgmv_shrink(lora_pool* p, const lora_plan* pl, int32_t slice, c
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
   const IoDesc io = p->io(slice, x, nullptr);
   const PlanLayout* lay = nullptr;
-  if (pl->n_mfma > 0) LORA_TRY(plan_layout(pl, single_io(io), (hipStream_t)stream, &lay));
-  return hip_status(launch_sgmv_shrink(p->dtype, p->view(), pl->view(lay), io, v, v_ld, (hipStream_t)stream),
+  LORA_TRY(find_layout(pl, single_io(io), ws, ws_bytes, true, &lay));
+  LORA_TRY(check_pool(p));
+  return hip_status(launch_sgmv_shrink(p->dtype, p->view(), pl->view(lay, ws), io, v, v_ld,
+                                       (hipStream_t)stream),
                     "sgmv_shrink");
 }
 
@@ -157,24 +180,26 @@ lora_status lora_sgmv_expand(lora_pool* p, const lora_plan* pl, int32_t slice, c
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
   const IoDesc io = p->io(slice, nullptr, y);
   const PlanLayout* lay = nullptr;
-  if (pl->n_mfma > 0) LORA_TRY(plan_layout(pl, single_io(io), (hipStream_t)stream, &lay));
-  return hip_status(launch_sgmv_expand(p->dtype, y_dtype, p->view(), pl->view(lay), io, v, v_ld,
+  LORA_TRY(find_layout(pl, single_io(io), nullptr, 0, false, &lay));
+  return hip_status(launch_sgmv_expand(p->dtype, y_dtype, p->view(), pl->view(lay, nullptr), io, v, v_ld,
                                        (hipStream_t)stream),
                     "sgmv_expand");
 }
 
 lora_status lora_apply(lora_pool* p, const lora_plan* pl, int32_t n_io, const lora_io* io,
-                       int32_t y_dtype, void* stream) {
+                       int32_t y_dtype, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  LORA_TRY(check_pool(p));
+  if (!p) return fail(LORA_E_ARG, "null pool");
   LORA_TRY(check_plan(p, pl));
   LORA_TRY(check_ydt(p, y_dtype));
   IoSet ios;
   LORA_TRY(build_ioset(p, n_io, io, ios));
   if (pl->n_tokens == 0) return LORA_OK;
   const PlanLayout* lay = nullptr;
-  if (pl->n_mfma > 0) LORA_TRY(plan_layout(pl, ios, (hipStream_t)stream, &lay));
-  return hip_status(launch_apply(p->dtype, y_dtype, p->view(), pl->view(lay), ios, (hipStream_t)stream),
+  LORA_TRY(find_layout(pl, ios, ws, ws_bytes, true, &lay));
+  LORA_TRY(check_pool(p));
+  return hip_status(launch_apply(p->dtype, y_dtype, p->view(), pl->view(lay, ws), ios,
+                                 (hipStream_t)stream),
                     "apply");
 }
 

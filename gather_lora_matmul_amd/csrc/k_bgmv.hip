@@ -26,7 +26,7 @@ __global__ __launch_bounds__(NT) void k_bgmv_shrink(PoolView pv, IoDesc io,
   const int a = ids[i];
   DevEntry e;
   e.rank = 0;
-  if (a >= 0) e = pv.entries[io.slice * pv.max_adapters + a];
+  if (adapter_in_table(pv, a)) e = pv.entries[io.slice * pv.max_adapters + a];
   const int k_lo = grp * rpg;
   const int k_end = min(k_lo + rpg, v_ld);
   const int k_hi = max(k_lo, min(e.rank, k_end));
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(NT) void k_bgmv_expand(PoolView pv, IoDesc io,
   xcd_unit_split(blockIdx.x, nsplit, i, q);
   if (i >= n) return;
   const int a = ids[i];
-  if (a < 0) return;
+  if (!adapter_in_table(pv, a)) return;
   const DevEntry e = pv.entries[io.slice * pv.max_adapters + a];
   if (e.rank <= 0) return;
   const int m_lo = q * rps;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
   const int i = unit - io_i * n;
   const IoDesc io = ios.io[io_i];
   const int a = ids[i];
-  if (a < 0) return;
+  if (!adapter_in_table(pv, a)) return;
   const DevEntry e = pv.entries[io.slice * pv.max_adapters + a];
   if (e.rank <= 0) return;
   const int m_lo = q * rps;

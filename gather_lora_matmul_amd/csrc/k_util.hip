@@ -63,7 +63,7 @@ __global__ void k_debug_resolve(PoolView pv, IoDesc io, int max_rank, int elt,
   const int a = ids[i];
   DevEntry e;
   e.rank = 0;
-  if (a >= 0) e = pv.entries[io.slice * pv.max_adapters + a];
+  if (adapter_in_table(pv, a)) e = pv.entries[io.slice * pv.max_adapters + a];
   const int na = max_rank * io.npa;
   for (int idx = threadIdx.x; idx < na; idx += blockDim.x) {
     const int k = idx / io.npa;

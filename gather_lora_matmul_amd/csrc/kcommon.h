@@ -173,6 +173,13 @@ __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
 }
 
 // ---- page-table resolution ---------------------------------------------------
+// A device id names an adapter iff it lies in [0, max_adapters); negative ids
+// (no adapter) and ids past the table are both skipped, so a bad id never
+// indexes past the adapter table.
+__device__ __forceinline__ bool adapter_in_table(const PoolView& pv, int a) {
+  return (unsigned)a < (unsigned)pv.max_adapters;
+}
+
 // Load of a wave-uniform index of a read-only table through the scalar cache:
 // the pointer is cast to the constant address space, so the load is an s_load
 // tracked by its own counter and never waits behind outstanding vector loads.
@@ -211,8 +218,10 @@ __device__ __forceinline__ int64_t b_offset(const PoolView& pv, const DevEntry& 
 }
 
 // Byte offset of B row m for a lane of a wave whose rows all lie in
-// [m0, m0 + 64), m0 wave-uniform: with rpp >= 64 those rows touch at most two
-// pages, whose ids are read with scalar loads (q_last bounds the page list).
+// [m0, m0 + 16), m0 wave-uniform (the MFMA expand's 16-row groups): with
+// rpp >= 16 (the planner only makes tiles of such layouts) those rows touch at
+// most two pages, whose ids are read with scalar loads (q_last bounds the page
+// list).
 __device__ __forceinline__ int64_t b_offset_wave(const PoolView& pv, const DevEntry& e, int elt,
                                                  int m, int m0, int q_last) {
   int q0 = (int)((float)m0 * e.inv_rpp);

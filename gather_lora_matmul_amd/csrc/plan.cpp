@@ -28,86 +28,106 @@ namespace lora {
 constexpr int64_t kPieceSetupShrink = 600;
 constexpr int64_t kPieceSetupExpand = 1800;
 
-lora_status plan_layout(const lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out) {
+std::vector<int32_t> layout_key(const IoSet& ios) {
+  std::vector<int32_t> key;
+  key.push_back(ios.n_io);
+  for (int j = 0; j < ios.n_io; ++j) {
+    key.push_back((ios.io[j].d_in + 63) / 64);
+    key.push_back((ios.io[j].d_out + 63) / 64);
+  }
+  return key;
+}
+
+const PlanLayout* plan_find_layout(const lora_plan* pl, const IoSet& ios) {
+  const std::vector<int32_t> key = layout_key(ios);
+  for (const PlanLayout& l : pl->layouts)
+    if (l.valid && l.key == key) {
+      const_cast<PlanLayout&>(l).used = ++pl->layout_clock;
+      return &l;
+    }
+  return nullptr;
+}
+
+lora_status plan_prepare_layout(lora_plan* pl, const IoSet& ios, hipStream_t s) {
+  if (plan_find_layout(pl, ios)) return LORA_OK;
   const int J = ios.n_io;
-  const int T = pl->n_mfma;
   const int G = pl->G;
   std::vector<int32_t> nst((size_t)J), nch((size_t)J);
-  std::vector<int32_t> key;
-  key.push_back(J);
   for (int j = 0; j < J; ++j) {
     nst[(size_t)j] = (ios.io[j].d_in + 63) / 64;
     nch[(size_t)j] = (ios.io[j].d_out + 63) / 64;
-    key.push_back(nst[(size_t)j]);
-    key.push_back(nch[(size_t)j]);
   }
-  PlanLayout* lay = nullptr;
+  // build into the least recently used slot
+  PlanLayout* lay = &pl->layouts[0];
   for (PlanLayout& l : pl->layouts)
-    if (l.valid && l.key == key) lay = &l;
-  if (!lay) {
-    // build: the least recently used slot
-    lay = &pl->layouts[0];
-    for (PlanLayout& l : pl->layouts)
-      if (!l.valid || l.used < lay->used) lay = &l;
-    lay->valid = false;
-    LayoutHost h;
-    if (!layout_host(pl->h_ws, pl->h_we, pl->h_tu, nst, nch, G, kPieceSetupShrink,
-                     kPieceSetupExpand, h))
-      return fail(LORA_E_ARG, "plan: partial-tile workspace exceeds 2^31 float4 units");
-    const std::vector<int32_t>& buf = h.buf;
-    const int64_t units = h.part_units;
-    const size_t bytes = sizeof(int32_t) * buf.size();
-    if (lay->ev_pending) {  // the staging buffer of this slot may still be copied from
-      LORA_HIP(hipEventSynchronize(lay->ev));
-      lay->ev_pending = false;
-    }
-    if (bytes > lay->cap) {
-      if (lay->d_buf) {
-        LORA_HIP(hipDeviceSynchronize());  // earlier launches may still read it
-        (void)hipFree(lay->d_buf);
-        lay->d_buf = nullptr;
-      }
-      if (lay->h_buf) (void)hipHostFree(lay->h_buf);
-      lay->h_buf = nullptr;
-      lay->cap = 0;
-      const size_t cap = bytes + bytes / 2 + 4096;
-      LORA_HIP(hipMalloc((void**)&lay->d_buf, cap));
-      hipError_t e = hipHostMalloc((void**)&lay->h_buf, cap, hipHostMallocDefault);
-      if (e != hipSuccess) {
-        (void)hipFree(lay->d_buf);
-        lay->d_buf = nullptr;
-        return fail(LORA_E_HIP, "plan layout staging: %s", hipGetErrorString(e));
-      }
-      lay->cap = cap;
-    }
-    if (!lay->ev) LORA_HIP(hipEventCreateWithFlags(&lay->ev, hipEventDisableTiming));
-    memcpy(lay->h_buf, buf.data(), bytes);
-    LORA_HIP(hipMemcpyAsync(lay->d_buf, lay->h_buf, bytes, hipMemcpyHostToDevice, s));
-    LORA_HIP(hipEventRecord(lay->ev, s));
-    lay->ev_pending = true;
-    lay->key = key;
-    lay->part_units = units;
-    lay->o_bs = h.o_bs;
-    lay->o_be = h.o_be;
-    lay->o_fl = h.o_fl;
-    lay->o_off = h.o_off;
-    lay->o_ent = h.o_ent;
+    if (!l.valid || l.used < lay->used) lay = &l;
+  lay->valid = false;
+  LayoutHost h;
+  if (!layout_host(pl->h_ws, pl->h_we, pl->h_tu, nst, nch, G, kPieceSetupShrink,
+                   kPieceSetupExpand, h))
+    return fail(LORA_E_ARG, "plan: partial-tile workspace exceeds 2^31 float4 units");
+  const std::vector<int32_t>& buf = h.buf;
+  const size_t bytes = sizeof(int32_t) * buf.size();
+  if (pl->pool->host_only) {  // sizes only: nothing runs on a host-only pool
+    lay->key = layout_key(ios);
+    lay->part_units = h.part_units;
     lay->valid = true;
+    lay->used = ++pl->layout_clock;
+    return LORA_OK;
   }
-  lay->used = ++pl->layout_clock;
-  // partial-tile workspace
-  const size_t need = 4 * (size_t)lay->part_units;  // floats
-  if (need > pl->part_cap) {
-    if (pl->d_part) {
-      LORA_HIP(hipDeviceSynchronize());  // earlier launches may still use the old buffer
-      (void)hipFree(pl->d_part);
-      pl->d_part = nullptr;
-      pl->part_cap = 0;
+  if (lay->ev_pending) {  // the staging buffer of this slot may still be copied from
+    LORA_HIP(hipEventSynchronize(lay->ev));
+    lay->ev_pending = false;
+  }
+  if (bytes > lay->cap) {
+    if (lay->d_buf) {
+      LORA_HIP(hipDeviceSynchronize());  // earlier launches may still read it
+      (void)hipFree(lay->d_buf);
+      lay->d_buf = nullptr;
     }
-    LORA_HIP(hipMalloc((void**)&pl->d_part, sizeof(float) * need));
-    pl->part_cap = need;
+    if (lay->h_buf) (void)hipHostFree(lay->h_buf);
+    lay->h_buf = nullptr;
+    lay->cap = 0;
+    const size_t cap = bytes + bytes / 2 + 4096;
+    LORA_HIP(hipMalloc((void**)&lay->d_buf, cap));
+    hipError_t e = hipHostMalloc((void**)&lay->h_buf, cap, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      (void)hipFree(lay->d_buf);
+      lay->d_buf = nullptr;
+      return fail(LORA_E_HIP, "plan layout staging: %s", hipGetErrorString(e));
+    }
+    lay->cap = cap;
   }
-  *out = lay;
+  if (!lay->ev) LORA_HIP(hipEventCreateWithFlags(&lay->ev, hipEventDisableTiming));
+  memcpy(lay->h_buf, buf.data(), bytes);
+  LORA_HIP(hipMemcpyAsync(lay->d_buf, lay->h_buf, bytes, hipMemcpyHostToDevice, s));
+  LORA_HIP(hipEventRecord(lay->ev, s));
+  lay->ev_pending = true;
+  lay->key = layout_key(ios);
+  lay->part_units = h.part_units;
+  lay->o_bs = h.o_bs;
+  lay->o_be = h.o_be;
+  lay->o_fl = h.o_fl;
+  lay->o_off = h.o_off;
+  lay->o_ent = h.o_ent;
+  lay->valid = true;
+  lay->used = ++pl->layout_clock;
+  return LORA_OK;
+}
+
+// Launch shape of a prepare / workspace-size call: the slices of io (x and y
+// are not read).
+lora_status shape_of(const lora_plan* pl, int32_t n_io, const lora_io* io, IoSet& ios) {
+  if (!pl || !pl->built) return fail(LORA_E_ARG, "plan not built");
+  if (n_io < 1 || n_io > LORA_MAX_IO || !io) return fail(LORA_E_ARG, "n_io must be in [1, %d]", LORA_MAX_IO);
+  const lora_pool* p = pl->pool;
+  memset(&ios, 0, sizeof(ios));
+  ios.n_io = n_io;
+  for (int k = 0; k < n_io; ++k) {
+    if (io[k].slice < 0 || io[k].slice >= p->n_slices)
+      return fail(LORA_E_ARG, "io %d: slice %d out of range", k, io[k].slice);
+    ios.io[k] = p->io(io[k].slice, nullptr, nullptr);
+  }
   return LORA_OK;
 }
 
@@ -125,6 +145,8 @@ lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** ou
   pl->max_tokens = max_tokens;
   pl->h_perm.reserve((size_t)max_tokens);
   pl->h_items.reserve((size_t)max_tokens);
+  // host-only pools (layout tests): the nominal grid of a 256-CU device
+  if (pool->host_only) pl->G = 512;
   if (!pool->host_only) {
     // persistent MFMA kernels run two blocks per compute unit
     int ncu = 0;
@@ -163,10 +185,9 @@ lora_status lora_plan_destroy(lora_plan* pl) {
       (void)hipEventDestroy(l.ev);
     }
   if (pl->h_pinned) (void)hipHostFree(pl->h_pinned);
-  if (pl->d_perm || pl->d_part) (void)hipDeviceSynchronize();  // launches may still read them
+  if (pl->d_perm) (void)hipDeviceSynchronize();  // launches may still read the plan's buffers
   if (pl->d_perm) (void)hipFree(pl->d_perm);
   if (pl->d_items) (void)hipFree(pl->d_items);
-  if (pl->d_part) (void)hipFree(pl->d_part);
   for (PlanLayout& l : pl->layouts) {
     if (l.d_buf) (void)hipFree(l.d_buf);
     if (l.h_buf) (void)hipHostFree(l.h_buf);
@@ -304,6 +325,30 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
     pl->ev_pending = true;
   }
   pl->built = true;
+  return LORA_OK;
+}
+
+lora_status lora_plan_prepare(lora_plan* pl, int32_t n_io, const lora_io* io, void* stream) {
+  clear_error();
+  IoSet ios;
+  lora_status st = shape_of(pl, n_io, io, ios);
+  if (st) return st;
+  if (pl->n_mfma == 0) return LORA_OK;  // nothing to lay out
+  return plan_prepare_layout(pl, ios, (hipStream_t)stream);
+}
+
+lora_status lora_workspace_size(const lora_plan* pl, int32_t n_io, const lora_io* io,
+                                size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(LORA_E_ARG, "null bytes");
+  IoSet ios;
+  lora_status st = shape_of(pl, n_io, io, ios);
+  if (st) return st;
+  *bytes = 0;
+  if (pl->n_mfma == 0) return LORA_OK;
+  const PlanLayout* lay = plan_find_layout(pl, ios);
+  if (!lay) return fail(LORA_E_STATE, "launch shape not prepared: call lora_plan_prepare");
+  *bytes = 16 * (size_t)lay->part_units;
   return LORA_OK;
 }
 

@@ -98,9 +98,8 @@ struct lora_pool {
 struct lora_plan;
 namespace lora {
 // The range tables and split-K contributions of one launch shape (n_io, then
-// the stage and chunk counts of each launch slice), built on the host at the
-// first launch of that shape after a plan build and copied to the device on
-// the launch stream.
+// the stage and chunk counts of each launch slice), built on the host by
+// lora_plan_prepare and copied to the device on its stream.
 struct PlanLayout {
   std::vector<int32_t> key;
   bool valid = false;
@@ -113,11 +112,17 @@ struct PlanLayout {
   int64_t part_units = 0;     // float4 units of partial tiles
   size_t o_bs = 0, o_be = 0, o_fl = 0, o_off = 0, o_ent = 0;  // int32 offsets
 };
-constexpr int kPlanLayouts = 4;
+constexpr int kPlanLayouts = 8;
 
-// Layout for the launch slices of `ios` (built and uploaded on `s` if the plan
-// has none of that shape), with the plan's partial-tile workspace grown to it.
-lora_status plan_layout(const lora_plan* pl, const IoSet& ios, hipStream_t s, const PlanLayout** out);
+// Key of a launch shape: n_io, then per launch slice its shrink stage and
+// expand chunk counts.
+std::vector<int32_t> layout_key(const IoSet& ios);
+// Build (or find) the layout of this launch shape: host work, may allocate and
+// synchronise (lora_plan_prepare only).
+lora_status plan_prepare_layout(lora_plan* pl, const IoSet& ios, hipStream_t s);
+// The prepared layout of this launch shape, or null (compute calls: no
+// allocation, no synchronisation).
+const PlanLayout* plan_find_layout(const lora_plan* pl, const IoSet& ios);
 }  // namespace lora
 
 struct lora_plan {
@@ -144,13 +149,12 @@ struct lora_plan {
   std::vector<int32_t> h_ws;  // per MFMA tile: weight of one shrink stage
   std::vector<int32_t> h_we;  //   ... of one expand chunk
   std::vector<int32_t> h_tu;  //   ... float4 units of one partial tile
-  // Launch-time state of a built plan (compute calls take the plan as const):
-  // the cache of launch-shape layouts and the partial-tile workspace.
-  mutable lora::PlanLayout layouts[lora::kPlanLayouts];
+  // Launch shapes prepared for this build (lora_plan_prepare).  The LRU stamp
+  // is bumped by compute calls, which take the plan as const.
+  lora::PlanLayout layouts[lora::kPlanLayouts];
   mutable uint64_t layout_clock = 0;
-  mutable float* d_part = nullptr;  // partial tiles, grown on demand
-  mutable size_t part_cap = 0;      // floats
-  lora::PlanView view(const lora::PlanLayout* lay) const {
+  // part: the caller's workspace for the partial tiles of this call
+  lora::PlanView view(const lora::PlanLayout* lay, void* part) const {
     lora::PlanView v;
     v.items = d_items;
     v.perm = d_perm;
@@ -159,7 +163,7 @@ struct lora_plan {
     v.part_fl = lay ? reinterpret_cast<const int2*>(lay->d_buf + lay->o_fl) : nullptr;
     v.c_off = lay ? lay->d_buf + lay->o_off : nullptr;
     v.c_ent = lay ? lay->d_buf + lay->o_ent : nullptr;
-    v.part = d_part;
+    v.part = reinterpret_cast<float*>(part);
     v.n_items = n_items;
     v.n_tokens = n_tokens;
     v.n_mfma = n_mfma;

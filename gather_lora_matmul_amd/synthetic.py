@@ -12,7 +12,8 @@ from typing import Iterable, Optional
 import numpy as np
 
 from . import (LORA_POOL_HOST_ONLY, LORA_POOL_POISON, DTYPE_CODE, lora_page_table_build,
-               lora_pool_alloc_pages, lora_pool_create, lora_pool_destroy, lora_pool_upload)
+               lora_plan_prepare, lora_pool_alloc_pages, lora_pool_create, lora_pool_destroy,
+               lora_pool_upload, lora_workspace_size)
 
 _TORCH_DT = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 
@@ -38,6 +39,20 @@ def from_device(t, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return c.to(torch.float32).numpy()
     return c.view(torch.int16).numpy().view(np.uint16)
+
+
+def prepare_shapes(plan: int, shapes, stream=None):
+    """Prepare the launch shapes (lists of slices) of a built plan and allocate
+    one device workspace large enough for all of them (torch uint8, or None if
+    none needs any).  Returns the workspace."""
+    import torch
+    need = 0
+    for sl in shapes:
+        lora_plan_prepare(plan, list(sl), stream=stream)
+        need = max(need, lora_workspace_size(plan, list(sl)))
+    if need == 0:
+        return None
+    return torch.empty(need, dtype=torch.uint8, device="cuda")
 
 
 class SyntheticPool:

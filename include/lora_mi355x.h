@@ -25,14 +25,17 @@
  *   - Pointers named *_dev are device pointers (HBM), *_host are host pointers.
  *     The caller owns every buffer it passes in; the library never frees them.
  *   - `stream` is a hipStream_t (NULL: the null stream).  Compute entry points
- *     are stream-ordered and never synchronise the host.
+ *     (lora_bgmv_*, lora_sgmv_*, lora_apply) are stream-ordered: they neither
+ *     allocate memory nor wait for the device.  Set-up calls (pool creation,
+ *     upload, evict, page-table build, plan create/build/prepare) may do both.
  *   - x rows are d_in elements of the pool dtype, y rows d_out elements of
  *     y_dtype (the pool dtype or LORA_F32), both dense row-major, 16-byte
  *     aligned base pointers.  v (the shrink output) is fp32 [n][v_ld].
- *   - Adapter ids on the device must lie in [-1, max_adapters) and name
- *     adapters resident in the slice used; this is a contract the kernels do
- *     not check (a non-resident adapter contributes nothing).  Host-side ids
- *     (lora_plan_build) are checked.
+ *   - Adapter ids on the device should lie in [-1, max_adapters) and name
+ *     adapters resident in the slice used.  The kernels treat any id outside
+ *     [0, max_adapters) like -1 (the token is skipped) and a non-resident
+ *     adapter as contributing nothing; no error is reported from the device.
+ *     Host-side ids (lora_plan_build) are checked.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H
@@ -183,14 +186,8 @@ typedef struct {
 } lora_plan_stats;
 
 /* Plan for up to max_tokens tokens (perm and item buffers allocated here).
- * On 16-bit pools the MFMA tiles also need, per launch shape (the slices of a
- * call), block-range tables and split-K contribution lists -- built on the
- * host at the first call of that shape after lora_plan_build and copied on the
- * call's stream; the plan keeps four shapes -- and a workspace of partial
- * tiles (16 bytes per token block x rank block x 64 per contribution, a few
- * MB), grown at first use (growing synchronizes the device).  A plan is used
- * by one stream and one host thread at a time: calls that use the same plan
- * must not overlap (they share its workspace and layout cache). */
+ * A plan is used by one stream and one host thread at a time: its set-up calls
+ * and the compute calls that use it are issued in order on one stream. */
 lora_status lora_plan_create(lora_pool* pool, int32_t max_tokens, lora_plan** out);
 lora_status lora_plan_destroy(lora_plan* plan);
 /* Build the plan of one batch from host ids [n] (any order, -1 = no adapter):
@@ -200,10 +197,29 @@ lora_status lora_plan_destroy(lora_plan* plan);
  * <= 4 tokens on the vector ALUs; items ordered MFMA first, then by rank band,
  * largest first.  Every id >= 0 must be < max_adapters and resident in every
  * slice (LORA_E_NOT_RESIDENT otherwise).  The plan is copied to the device on
- * `stream`; the host ids may be reused on return.  The SGMV calls below launch
- * one kernel per item kind present in the plan. */
+ * `stream`; the host ids may be reused on return.  Building drops the launch
+ * shapes prepared for the previous batch.  The SGMV calls below launch one
+ * kernel per item kind present in the plan. */
 lora_status lora_plan_build(lora_plan* plan, const int32_t* ids_host, int32_t n,
                             int32_t l_long, void* stream);
+/* Prepare one launch shape of a built plan: the slices of a planned call, in
+ * the order the call lists them (only io[k].slice is read; the split calls use
+ * one-slice shapes).  On 16-bit pools with MFMA tiles this builds, on the host,
+ * the block-range tables and split-K contribution lists of that shape and
+ * copies them to the device on `stream` (the plan keeps up to 8 shapes, least
+ * recently used replaced first); otherwise it does nothing.  Every planned
+ * compute call needs its shape prepared after the last lora_plan_build
+ * (LORA_E_STATE otherwise).  May allocate and synchronise. */
+lora_status lora_plan_prepare(lora_plan* plan, int32_t n_io, const lora_io* io_host,
+                              void* stream);
+/* Bytes of caller-owned device workspace that lora_apply and lora_sgmv_shrink
+ * need for this prepared launch shape: the split-K partial tiles of the MFMA
+ * tiles, 16 bytes per (token block x 16-rank block x 64 lanes) per
+ * contribution (a few MB at the configured workloads); 0 without MFMA tiles.
+ * The workspace needs no initial contents; calls that share one workspace must
+ * not overlap.  LORA_E_STATE if the shape is not prepared. */
+lora_status lora_workspace_size(const lora_plan* plan, int32_t n_io, const lora_io* io_host,
+                                size_t* bytes);
 lora_status lora_plan_get_stats(const lora_plan* plan, lora_plan_stats* out);
 /* Host copy of the plan: perm [n_tokens] (token indices, grouped by adapter)
  * and items [n_items][4] = {adapter, start in perm, count, kind (0 short,
@@ -213,19 +229,26 @@ lora_status lora_plan_export(const lora_plan* plan, int32_t* perm_host, int32_t*
 /* Shrink for a planned batch: v[i][.] as lora_bgmv_shrink (rows indexed by the
  * original token index).  MFMA tiles: two launches (block ranges, then the sum
  * of the partial tiles of every tile that several ranges share, in block
- * order). */
+ * order); the partial tiles go to workspace_dev (16-byte aligned, at least
+ * lora_workspace_size bytes for the one-slice shape {slice}, else LORA_E_ARG;
+ * may be NULL when that size is 0). */
 lora_status lora_sgmv_shrink(lora_pool* pool, const lora_plan* plan, int32_t slice,
-                             const void* x_dev, float* v_dev, int32_t v_ld, void* stream);
-/* Expand for a planned batch: y[i] += s B v[i]. */
+                             const void* x_dev, float* v_dev, int32_t v_ld, void* workspace_dev,
+                             size_t ws_bytes, void* stream);
+/* Expand for a planned batch: y[i] += s B v[i].  Needs the one-slice shape
+ * {slice} prepared; uses no workspace. */
 lora_status lora_sgmv_expand(lora_pool* pool, const lora_plan* plan, int32_t slice,
                              const float* v_dev, int32_t v_ld, void* y_dev, int32_t y_dtype,
                              void* stream);
 /* Fused shrink + expand for a planned (mixed prefill + decode) batch, for up to
  * LORA_MAX_IO slices; v is never materialized.  Short items: one launch, v in
  * LDS.  MFMA tiles: two launches on `stream` (shrink ranges keep partial tiles
- * in the plan's workspace; the expand sums them while loading V). */
+ * in workspace_dev; the expand sums them while loading V).  The launch shape
+ * (the io slices in this order) must be prepared; workspace_dev as for
+ * lora_sgmv_shrink, sized by lora_workspace_size for this shape. */
 lora_status lora_apply(lora_pool* pool, const lora_plan* plan, int32_t n_io,
-                       const lora_io* io_host, int32_t y_dtype, void* stream);
+                       const lora_io* io_host, int32_t y_dtype, void* workspace_dev,
+                       size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Debug / verification of the page-table resolution done inside the kernels.

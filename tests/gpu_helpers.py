@@ -20,9 +20,24 @@ def log(msg: str):
     sys.stdout.flush()
 
 
-def compare(y_gpu_bits: np.ndarray, y_ref: np.ndarray, y_dtype: str, what: str = ""):
+def _gate(got: np.ndarray, cmp: np.ndarray, ref_scale: float, what: str):
+    d = got - cmp
+    nrm = np.linalg.norm(cmp)
+    rel = np.linalg.norm(d) / nrm if nrm > 0 else np.linalg.norm(d)
+    mx = np.abs(d).max() if d.size else 0.0
+    bound = MAX_ABS * max(ref_scale, 1e-30)
+    assert rel <= REL_L2, "%s: rel L2 %.3e > %.1e" % (what, rel, REL_L2)
+    assert mx <= bound, "%s: max abs %.3e > %.3e" % (what, mx, bound)
+    return rel, mx
+
+
+def compare(y_gpu_bits: np.ndarray, y_ref: np.ndarray, y_dtype: str, what: str = "",
+            y0_bits: Optional[np.ndarray] = None):
     """Gate A (fp32 y): against the unrounded fp64 result.  Gate B (16-bit y):
-    against the oracle's result rounded once to the y dtype."""
+    against the oracle's result rounded once to the y dtype.  Every element of
+    the call is compared.  With fp32 y and a non-zero y0 (given as y0_bits) the
+    LoRA delta itself, y - y0, is also gated against the oracle's delta, so an
+    error in the delta cannot hide under the norm of y0."""
     if y_dtype == "f32":
         cmp = y_ref
     else:
@@ -30,14 +45,30 @@ def compare(y_gpu_bits: np.ndarray, y_ref: np.ndarray, y_dtype: str, what: str =
     g = W.dequantize(y_gpu_bits, y_dtype)
     assert g.shape == cmp.shape, (g.shape, cmp.shape)
     assert np.all(np.isfinite(g)), "%s: non-finite output (poisoned page read?)" % what
-    d = g - cmp
-    nrm = np.linalg.norm(cmp)
-    rel = np.linalg.norm(d) / nrm if nrm > 0 else np.linalg.norm(d)
-    mx = np.abs(d).max() if d.size else 0.0
-    bound = MAX_ABS * max(np.abs(y_ref).max() if y_ref.size else 0.0, 1e-30)
-    assert rel <= REL_L2, "%s: rel L2 %.3e > %.1e" % (what, rel, REL_L2)
-    assert mx <= bound, "%s: max abs %.3e > %.3e" % (what, mx, bound)
-    return rel, mx
+    out = _gate(g, cmp, np.abs(y_ref).max() if y_ref.size else 0.0, what)
+    if y0_bits is not None and y_dtype == "f32" and np.any(y0_bits != 0):
+        y0 = W.dequantize(y0_bits, "f32")
+        delta_ref = y_ref - y0
+        _gate(g - y0, delta_ref, np.abs(delta_ref).max() if delta_ref.size else 0.0,
+              what + " (delta y - y0)")
+    return out
+
+
+def compare_v(v_gpu: np.ndarray, v_ref: np.ndarray, ids: np.ndarray, ranks: np.ndarray,
+              what: str = ""):
+    """Split-API shrink output: v[i][k] for k < r_{a_i} within the gate of the
+    oracle's v; exact zeros for r_{a_i} <= k < v_ld and for tokens without an
+    adapter."""
+    assert v_gpu.shape == v_ref.shape, (v_gpu.shape, v_ref.shape)
+    n, v_ld = v_gpu.shape
+    r = np.where(ids >= 0, ranks[np.clip(ids, 0, None)], 0)
+    inside = np.arange(v_ld)[None, :] < r[:, None]
+    assert np.all(v_gpu[~inside] == 0), "%s: v not zero past the rank (%d elements)" % (
+        what, int(np.sum(v_gpu[~inside] != 0)))
+    g = v_gpu.astype(np.float64)[inside]
+    assert np.all(np.isfinite(g)), "%s: non-finite v" % what
+    if g.size:
+        _gate(g, v_ref[inside], np.abs(v_ref[inside]).max(), what + " (v)")
 
 
 def exact_compare(y_gpu_bits: np.ndarray, y_ref: np.ndarray, y_dtype: str, what: str = ""):
@@ -83,7 +114,12 @@ def ids_tensor(ids: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
 
 
+def oracle_threads() -> int:
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def reference(wl, batch, s: int, y_dtype: str, subset: Optional[Sequence[int]] = None,
-              threads: int = 8):
+              threads: Optional[int] = None, return_v: bool = False):
     return oracle.workload_reference(wl, batch, s, y_dtype=y_dtype, token_subset=subset,
-                                     n_threads=threads)
+                                     n_threads=threads or oracle_threads(), return_v=return_v)

@@ -247,3 +247,76 @@ def test_planner_rejects_bad_ids():
     assert e.value.status == -1
     L.lora_plan_destroy(plan)
     sp.close()
+
+
+def test_workspace_is_sized_per_prepared_shape_and_checked():
+    # A planned call needs its launch shape prepared after the plan build, and
+    # a caller-owned workspace of at least lora_workspace_size bytes: a short
+    # one is LORA_E_ARG before anything else happens.
+    wl = W.small_workload("bf16", 256, 520, [16, 64, 5], 256, n_slices=2)
+    ids = np.array([0] * 70 + [1] * 17 + [2] * 30 + [-1] * 3, np.int32)
+    sp, plan = _plan_for(wl, ids)
+    try:
+        assert L.lora_plan_get_stats(plan)["n_mfma_items"] > 0
+        with pytest.raises(L.LoraError) as e:
+            L.lora_workspace_size(plan, [0, 1])
+        assert e.value.status == -5  # not prepared
+        L.lora_plan_prepare(plan, [0, 1], stream=0)
+        L.lora_plan_prepare(plan, [1], stream=0)
+        need2 = L.lora_workspace_size(plan, [0, 1])
+        need1 = L.lora_workspace_size(plan, [1])
+        assert need2 > need1 > 0 and need2 % 16 == 0
+        # a shape is the sequence of the slices' dims: [1, 0] has those of [0, 1]
+        assert L.lora_workspace_size(plan, [1, 0]) == need2
+        fake = 1 << 20  # never dereferenced: every call below fails on the host
+        io = (L.Io * 2)(L.Io(0, 0, fake, fake), L.Io(1, 0, fake, fake))
+        lib = L.lib()
+        st = lib.lora_apply(sp.handle, plan, 2, io, L.LORA_BF16, fake, need2 - 16, None)
+        assert st == -1 and "workspace" in L.lora_last_error()
+        st = lib.lora_apply(sp.handle, plan, 2, io, L.LORA_BF16, None, need2, None)
+        assert st == -1
+        st = lib.lora_apply(sp.handle, plan, 2, io, L.LORA_BF16, fake + 8, need2, None)
+        assert st == -1 and "aligned" in L.lora_last_error()
+        st = lib.lora_sgmv_shrink(sp.handle, plan, 1, fake, fake, 64, fake, need1 - 16, None)
+        assert st == -1
+        # enough workspace: the host-only pool is refused only now
+        st = lib.lora_apply(sp.handle, plan, 2, io, L.LORA_BF16, fake, need2, None)
+        assert st == -5 and "host-only" in L.lora_last_error()
+        # a new build drops the prepared shapes
+        L.lora_plan_build(plan, ids[:50], stream=0)
+        with pytest.raises(L.LoraError) as e:
+            L.lora_workspace_size(plan, [0, 1])
+        assert e.value.status == -5
+        st = lib.lora_apply(sp.handle, plan, 2, io, L.LORA_BF16, fake, need2, None)
+        assert st == -5 and "prepare" in L.lora_last_error()
+    finally:
+        L.lora_plan_destroy(plan)
+        sp.close()
+
+
+def test_binding_checks_buffers_before_the_call():
+    # The C ABI takes raw pointers; the binding checks element types and sizes
+    # first (host tensors suffice: nothing reaches the library).
+    torch = pytest.importorskip("torch")
+    wl = W.small_workload("bf16", 64, 128, [8, 8], 64, n_slices=2)
+    with _host_pool(wl) as sp:
+        n = 5
+        x = torch.zeros((n, 64), dtype=torch.bfloat16)
+        y = torch.zeros((n, 128), dtype=torch.bfloat16)
+        ids64 = torch.zeros(n, dtype=torch.int64)
+        ids = torch.zeros(n, dtype=torch.int32)
+        with pytest.raises(TypeError, match="int32"):
+            L.lora_bgmv_apply(sp.handle, [(0, x, y)], ids64, L.LORA_BF16)
+        with pytest.raises(TypeError, match="dtype"):
+            L.lora_bgmv_apply(sp.handle, [(0, x.float(), y)], ids, L.LORA_BF16)
+        with pytest.raises(TypeError, match="dtype"):
+            L.lora_bgmv_apply(sp.handle, [(0, x, y)], ids, L.LORA_F32)
+        with pytest.raises(ValueError, match="elements"):
+            L.lora_bgmv_apply(sp.handle, [(1, x, y[:4])], ids, L.LORA_BF16)
+        with pytest.raises(ValueError, match="elements"):
+            L.lora_bgmv_shrink(sp.handle, 0, x[:3], ids, torch.zeros((n, 8)))
+        with pytest.raises(ValueError, match="elements"):
+            L.lora_bgmv_expand(sp.handle, 0, torch.zeros((n, 4)), ids, y, L.LORA_BF16, v_ld=8)
+        with pytest.raises(TypeError, match="dtype"):
+            L.lora_bgmv_expand(sp.handle, 0, torch.zeros((n, 8), dtype=torch.float64), ids, y,
+                               L.LORA_BF16)
