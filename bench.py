@@ -177,25 +177,29 @@ class Runner:
             self.plan_host["plan_build_us"] = float(np.median(t_build)) * 1e6
             self.plan_host["prepare_us"] = float(np.median(t_prep)) * 1e6
         self.stream = torch.cuda.current_stream()
+        self.stream_h = self.stream.cuda_stream
+        # fused steps: arguments checked and marshalled once per rotating batch
+        self.calls = []
+        if mode == "fused":
+            for k, b in enumerate(self.batches):
+                io = [(s, self.xs[k][j], self.ys[k][j]) for j, s in enumerate(slices)]
+                self.calls.append(
+                    L.prepare_apply(self.sp.handle, self.plans[k], io, self.ydt, workspace=self.wss[k])
+                    if self.planned else L.prepare_bgmv_apply(self.sp.handle, io, self.ids_d[k], self.ydt))
         self.entry = (("lora_apply" if self.planned else "lora_bgmv_apply") if mode == "fused"
                       else ("lora_sgmv_shrink+expand" if self.planned else "lora_bgmv_shrink+expand"))
         self.src_hash = source_hash(PLANNED_SOURCES if self.planned else BGMV_SOURCES)
 
     def step(self, i: int):
         L, k = self.L, i % len(self.batches)
-        io = [(s, self.xs[k][j], self.ys[k][j]) for j, s in enumerate(self.slices)]
-        if self.planned:
-            if self.mode == "fused":
-                L.lora_apply(self.sp.handle, self.plans[k], io, self.ydt, workspace=self.wss[k],
-                             stream=self.stream)
-            else:
-                for j, s in enumerate(self.slices):
-                    L.lora_sgmv_shrink(self.sp.handle, self.plans[k], s, self.xs[k][j], self.v[j],
-                                       workspace=self.wss[k], stream=self.stream)
-                    L.lora_sgmv_expand(self.sp.handle, self.plans[k], s, self.v[j],
-                                       self.ys[k][j], self.ydt, stream=self.stream)
-        elif self.mode == "fused":
-            L.lora_bgmv_apply(self.sp.handle, io, self.ids_d[k], self.ydt, stream=self.stream)
+        if self.calls:  # fused: one prepared call
+            self.calls[k](self.stream_h)
+        elif self.planned:
+            for j, s in enumerate(self.slices):
+                L.lora_sgmv_shrink(self.sp.handle, self.plans[k], s, self.xs[k][j], self.v[j],
+                                   workspace=self.wss[k], stream=self.stream)
+                L.lora_sgmv_expand(self.sp.handle, self.plans[k], s, self.v[j],
+                                   self.ys[k][j], self.ydt, stream=self.stream)
         else:
             for j, s in enumerate(self.slices):
                 L.lora_bgmv_shrink(self.sp.handle, s, self.xs[k][j], self.ids_d[k], self.v[j],

@@ -435,6 +435,45 @@ def lora_apply(pool: int, plan: int, ios: Sequence[Tuple[int, object, object]], 
 
 
 # ----------------------------------------------------------------------------
+# prepared calls: arguments checked and marshalled once
+# ----------------------------------------------------------------------------
+class PreparedCall:
+    """A compute call whose buffers were checked and whose ctypes arguments were
+    built once; calling it only invokes the C entry point on `stream` (a raw
+    hipStream_t int, a torch stream, or None for torch's current stream).  The
+    tensors it was made from must stay alive and keep their storage."""
+
+    __slots__ = ("_fn", "_args", "_where", "_keep")
+
+    def __init__(self, fn, args, where, keep):
+        self._fn, self._args, self._where, self._keep = fn, tuple(args), where, keep
+
+    def __call__(self, stream=None):
+        st = self._fn(*self._args, stream if isinstance(stream, int) else _stream(stream))
+        if st != LORA_OK:
+            _check(st, self._where)
+
+
+def prepare_bgmv_apply(pool: int, ios: Sequence[Tuple[int, object, object]], ids,
+                       y_dtype: int) -> PreparedCall:
+    _check_ids(ids)
+    _check_io(pool, ios, int(ids.shape[0]), y_dtype)
+    arr = _ios(ios)
+    return PreparedCall(_lib.lora_bgmv_apply, (pool, len(ios), arr, _dev_ptr(ids),
+                                               int(ids.shape[0]), y_dtype),
+                        "lora_bgmv_apply", (ios, ids, arr))
+
+
+def prepare_apply(pool: int, plan: int, ios: Sequence[Tuple[int, object, object]], y_dtype: int,
+                  workspace=None) -> PreparedCall:
+    _check_io(pool, ios, _plan_tokens(plan), y_dtype)
+    arr = _ios(ios)
+    wp, wb = _ws(workspace)
+    return PreparedCall(_lib.lora_apply, (pool, plan, len(ios), arr, y_dtype, wp, wb),
+                        "lora_apply", (ios, workspace, arr))
+
+
+# ----------------------------------------------------------------------------
 # verification
 # ----------------------------------------------------------------------------
 def lora_debug_resolve(pool: int, slice_: int, ids, a_off, b_off, stream=None):
