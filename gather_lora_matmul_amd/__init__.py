@@ -35,7 +35,7 @@ EXPORTS = (
     "lora_pool_export_entry", "lora_pool_read_pages", "lora_bgmv_shrink", "lora_bgmv_expand",
     "lora_bgmv_apply", "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
     "lora_plan_get_stats", "lora_plan_export", "lora_plan_prepare", "lora_workspace_size",
-    "lora_sgmv_shrink", "lora_sgmv_expand", "lora_apply", "lora_debug_resolve",
+    "lora_sgmv_shrink", "lora_sgmv_expand", "lora_apply", "lora_apply_noalloc", "lora_debug_resolve",
     "lora_debug_gather", "lora_last_error",
 )
 
@@ -104,6 +104,7 @@ def _load() -> ctypes.CDLL:
         "lora_sgmv_shrink": [V, V, I32, V, V, I32, V, ctypes.c_size_t, V],
         "lora_sgmv_expand": [V, V, I32, V, I32, V, I32, V],
         "lora_apply": [V, V, I32, ctypes.POINTER(Io), I32, V, ctypes.c_size_t, V],
+        "lora_apply_noalloc": [V, V, I32, ctypes.POINTER(Io), I32, V],
         "lora_debug_resolve": [V, I32, V, I32, V, V, V],
         "lora_debug_gather": [V, I32, I32, V, V, V],
     }
@@ -432,6 +433,15 @@ def lora_apply(pool: int, plan: int, ios: Sequence[Tuple[int, object, object]], 
     wp, wb = _ws(workspace)
     _check(_lib.lora_apply(pool, plan, len(ios), arr, y_dtype, wp, wb, _stream(stream)),
            "lora_apply")
+
+
+def lora_apply_noalloc(pool: int, plan: int, ios: Sequence[Tuple[int, object, object]],
+                       y_dtype: int, stream=None):
+    """lora_apply with the library's static scratch as the workspace."""
+    _check_io(pool, ios, _plan_tokens(plan), y_dtype)
+    arr = _ios(ios)
+    _check(_lib.lora_apply_noalloc(pool, plan, len(ios), arr, y_dtype, _stream(stream)),
+           "lora_apply_noalloc")
 
 
 # ----------------------------------------------------------------------------

@@ -177,6 +177,14 @@ lora_status lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
     }
     p->owns_pages = true;
   }
+  {
+    const lora_status st = scratch_init(p->device);
+    if (st) {
+      if (p->owns_pages) (void)hipFree(p->pages);
+      delete p;
+      return st;
+    }
+  }
   e = hipMalloc((void**)&p->d_entries, sizeof(DevEntry) * p->slots.size());
   if (e == hipSuccess) e = hipMalloc((void**)&p->d_page_ids, sizeof(int32_t) * (size_t)p->n_pages);
   if (e == hipSuccess && poison) e = launch_fill_all(p->pages, bytes, nan_pattern(p->dtype), elt, nullptr);

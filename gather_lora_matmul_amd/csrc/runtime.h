@@ -18,6 +18,9 @@ struct Slot {
 
 lora_status fail(lora_status st, const char* fmt, ...);
 void clear_error();
+// Look up the device address of `device`'s static scratch array (device
+// current); done once per device, at pool creation.
+lora_status scratch_init(int device);
 
 #define LORA_HIP(expr)                                                                     \
   do {                                                                                     \

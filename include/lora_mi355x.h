@@ -250,6 +250,17 @@ lora_status lora_apply(lora_pool* pool, const lora_plan* plan, int32_t n_io,
                        const lora_io* io_host, int32_t y_dtype, void* workspace_dev,
                        size_t ws_bytes, void* stream);
 
+/* lora_apply for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels, with the partial tiles in a static device array of the library
+ * (16 MiB per GPU, held until the process ends) instead of a caller workspace.
+ * A launch shape whose lora_workspace_size exceeds 16 MiB is LORA_E_ARG.  The
+ * launch shape must be prepared as for lora_apply.  Every call on one GPU
+ * shares that GPU's array: calls on one GPU that overlap in time (other
+ * streams, other threads) race on it and must be serialised by the caller. */
+lora_status lora_apply_noalloc(lora_pool* pool, const lora_plan* plan, int32_t n_io,
+                               const lora_io* io_host, int32_t y_dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Debug / verification of the page-table resolution done inside the kernels.
  * ------------------------------------------------------------------------- */
