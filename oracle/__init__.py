@@ -23,7 +23,7 @@ _SRC = os.path.join(_HERE, "lora_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liblora_oracle.so")
 _lib = None
 
-DT = {"f32": 0, "f16": 1, "bf16": 2}
+DT = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
 
 
 def build(force: bool = True) -> str:
@@ -48,7 +48,8 @@ def _load():
     lib.oracle_decode.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P]
     lib.oracle_lora_apply.argtypes = [
         ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-        P, P, ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32]
+        ctypes.c_int32, P, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, ctypes.c_int32,
+        ctypes.c_int32]
     lib.oracle_walk_adapter.argtypes = [
         P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, P, P, P, P]
@@ -68,8 +69,12 @@ def max_threads() -> int:
     return int(_load().oracle_max_threads())
 
 
+def _storage(dtype: str):
+    return {"f32": np.float32, "e4m3": np.uint8}.get(dtype, np.uint16)
+
+
 def round_to(values: np.ndarray, dtype: str) -> np.ndarray:
-    """RNE-round float64 values to `dtype`; returns the stored form."""
+    """RNE-round float64 values to `dtype` (f32, f16, bf16); returns the stored form."""
     v = np.ascontiguousarray(values, dtype=np.float64)
     out = np.empty(v.shape, np.float32 if dtype == "f32" else np.uint16)
     rc = _load().oracle_round(_ptr(v), v.size, DT[dtype], _ptr(out))
@@ -88,13 +93,16 @@ def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def lora_apply(x_bits: np.ndarray, ids: np.ndarray, ranks: np.ndarray, scales: np.ndarray,
-               weights: Dict[int, Tuple[np.ndarray, np.ndarray]], y0_bits: np.ndarray,
+               weights: Dict[int, tuple], y0_bits: np.ndarray,
                w_dtype: str, y_dtype: str, return_v: bool = False, v_ld: int = 0,
-               n_threads: int = 1):
+               n_threads: int = 1, x_dtype: Optional[str] = None):
     """y_ref (float64 [n][d_out]) of y_i = y0_i + s_a B_a (A_a x_i).
 
-    `weights` maps adapter id -> (A bits [r][d_in], B bits [d_out][r]); only the
-    adapters that the batch names need to be present."""
+    `weights` maps adapter id -> (A bits [r][d_in], B bits [d_out][r]) or, for a
+    quantised adapter, (A codes, B codes, a_scale [r], b_scale [r]); only the
+    adapters that the batch names need to be present.  x is in x_dtype (default
+    w_dtype)."""
+    x_dtype = x_dtype or w_dtype
     x = np.ascontiguousarray(x_bits)
     y0 = np.ascontiguousarray(y0_bits)
     ids = np.ascontiguousarray(ids, np.int32)
@@ -106,15 +114,26 @@ def lora_apply(x_bits: np.ndarray, ids: np.ndarray, ranks: np.ndarray, scales: n
     na = ranks.shape[0]
     Ap = (ctypes.c_void_p * na)()
     Bp = (ctypes.c_void_p * na)()
+    SAp = (ctypes.c_void_p * na)()
+    SBp = (ctypes.c_void_p * na)()
+    quant = False
     keep = []
-    for a, (A, B) in weights.items():
-        A = np.ascontiguousarray(A)
-        B = np.ascontiguousarray(B)
+    for a, wt in weights.items():
+        A = np.ascontiguousarray(wt[0])
+        B = np.ascontiguousarray(wt[1])
         r = int(ranks[a])
         assert A.shape == (r, d_in) and B.shape == (d_out, r), (a, A.shape, B.shape, r)
         keep += [A, B]
         Ap[a] = _ptr(A)
         Bp[a] = _ptr(B)
+        if len(wt) == 4:
+            sa = np.ascontiguousarray(wt[2], np.float32)
+            sb = np.ascontiguousarray(wt[3], np.float32)
+            assert sa.shape == (r,) and sb.shape == (r,)
+            keep += [sa, sb]
+            SAp[a] = _ptr(sa)
+            SBp[a] = _ptr(sb)
+            quant = True
     y = np.empty((n, d_out), np.float64)
     if return_v:
         v_ld = v_ld or int(ranks.max())
@@ -122,10 +141,12 @@ def lora_apply(x_bits: np.ndarray, ids: np.ndarray, ranks: np.ndarray, scales: n
         vp = _ptr(v)
     else:
         v, vp = None, None
-    rc = _load().oracle_lora_apply(n, d_in, d_out, DT[w_dtype], DT[y_dtype], _ptr(x), _ptr(ids),
-                                   na, _ptr(ranks), _ptr(scales), ctypes.cast(Ap, ctypes.c_void_p),
-                                   ctypes.cast(Bp, ctypes.c_void_p), _ptr(y0), _ptr(y), vp, v_ld,
-                                   n_threads)
+    sa_arg = ctypes.cast(SAp, ctypes.c_void_p) if quant else None
+    sb_arg = ctypes.cast(SBp, ctypes.c_void_p) if quant else None
+    rc = _load().oracle_lora_apply(n, d_in, d_out, DT[w_dtype], DT[x_dtype], DT[y_dtype], _ptr(x),
+                                   _ptr(ids), na, _ptr(ranks), _ptr(scales),
+                                   ctypes.cast(Ap, ctypes.c_void_p), ctypes.cast(Bp, ctypes.c_void_p),
+                                   sa_arg, sb_arg, _ptr(y0), _ptr(y), vp, v_ld, n_threads)
     if rc == -1:
         raise KeyError("a token names an adapter whose weights were not supplied")
     if rc:
@@ -138,7 +159,7 @@ def walk_adapter(pool_bits: np.ndarray, dtype: str, page_elems: int, d_in: int, 
     """Rebuild dense (A, B) bits of one adapter slice from a host pool image."""
     pool = np.ascontiguousarray(pool_bits)
     n_pages = pool.size // page_elems
-    sd = np.float32 if dtype == "f32" else np.uint16
+    sd = _storage(dtype)
     A = np.empty((rank, d_in), sd)
     B = np.empty((d_out, rank), sd)
     ap = np.ascontiguousarray(a_pages, np.int32)
@@ -159,7 +180,7 @@ def workload_reference(wl, batch, slice_idx: int, y_dtype: Optional[str] = None,
                        return_v: bool = False):
     """Oracle result for one slice of a workload batch (optionally on a subset
     of tokens, for full-size sampled checks)."""
-    y_dtype = y_dtype or wl.dtype
+    y_dtype = y_dtype or wl.act_dtype
     x = batch.x[slice_idx]
     y0 = batch.y0[slice_idx]
     ids = batch.ids
@@ -167,7 +188,11 @@ def workload_reference(wl, batch, slice_idx: int, y_dtype: Optional[str] = None,
         sel = np.asarray(token_subset, np.int64)
         x, y0, ids = x[sel], y0[sel], ids[sel]
     used = sorted(set(int(a) for a in ids.tolist() if a >= 0))
-    weights = {a: wl.weights(a, slice_idx) for a in used}
+    weights = {}
+    for a in used:
+        A, B = wl.weights(a, slice_idx)
+        q = wl.qscales(a, slice_idx)
+        weights[a] = (A, B) if q is None else (A, B, q[0], q[1])
     return lora_apply(x, ids, wl.ranks, wl.scales, weights, y0, wl.dtype, y_dtype,
                       return_v=return_v, v_ld=wl.max_rank if return_v else 0,
-                      n_threads=n_threads)
+                      n_threads=n_threads, x_dtype=wl.act_dtype)

@@ -18,9 +18,13 @@
  *   of the multi-LoRA serving article (produtoramaxvision.com.br), whose naming
  *   is followed here (A = shrink r x d_in, B = expand d_out x r).
  *
- * Inputs arrive as raw storage bits (fp32, IEEE fp16 or bf16) and are decoded
- * exactly to double here, with this file's own decoders.  Sums run in ascending
- * index order in double.  The scale is the stored fp32 value.
+ * Inputs arrive as raw storage bits (fp32, IEEE fp16, bf16, or OCP FP8 E4M3
+ * codes for quantised adapters) and are decoded exactly to double here, with
+ * this file's own decoders.  Quantised adapters carry fp32 scales: one per rank
+ * row of A and one per rank column of B, so that the dequantised matrices are
+ *     A[k][j] = sa[k] * code(A)[k][j]      B[m][k] = code(B)[m][k] * sb[k]
+ * (each product exact in double).  Sums run in ascending index order in
+ * double.  The adapter scale s_a is the stored fp32 value.
  */
 #include <math.h>
 #include <stdint.h>
@@ -30,9 +34,9 @@
 #include <omp.h>
 #endif
 
-enum { ODT_F32 = 0, ODT_F16 = 1, ODT_BF16 = 2 };
+enum { ODT_F32 = 0, ODT_F16 = 1, ODT_BF16 = 2, ODT_E4M3 = 3 };
 
-static int elt_size(int32_t dt) { return dt == ODT_F32 ? 4 : 2; }
+static int elt_size(int32_t dt) { return dt == ODT_F32 ? 4 : (dt == ODT_E4M3 ? 1 : 2); }
 
 /* ---- exact decoders ---------------------------------------------------- */
 static double dec_f16(uint16_t h) {
@@ -54,8 +58,21 @@ static double dec_f32(const void* p) {
   memcpy(&f, p, 4);
   return (double)f;
 }
+/* OCP 8-bit floating point E4M3: sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits; exponent field 0 holds subnormals m/8 * 2^-6; no infinities; the codes
+ * with every exponent and mantissa bit set are NaN; the largest finite value is
+ * 1.75 * 2^8 = 448. */
+static double dec_e4m3(uint8_t b) {
+  const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
 static double dec_at(const void* base, int32_t dt, int64_t idx) {
   if (dt == ODT_F32) return dec_f32((const char*)base + 4 * idx);
+  if (dt == ODT_E4M3) return dec_e4m3(((const uint8_t*)base)[idx]);
   uint16_t h;
   memcpy(&h, (const char*)base + 2 * idx, 2);
   return dt == ODT_F16 ? dec_f16(h) : dec_bf16(h);
@@ -119,29 +136,33 @@ int oracle_round(const double* in, int64_t n, int32_t dt, void* out) {
 
 /* Decode n stored values to double. */
 int oracle_decode(const void* in, int64_t n, int32_t dt, double* out) {
-  if (dt < 0 || dt > 2) return -2;
+  if (dt < 0 || dt > 3) return -2;
   for (int64_t i = 0; i < n; ++i) out[i] = dec_at(in, dt, i);
   return 0;
 }
 
 /*
  * The LoRA apply, one token at a time.
- *   x_bits  [n][d_in]  in w_dtype        y0_bits [n][d_out] in y_dtype
+ *   x_bits  [n][d_in]  in x_dtype        y0_bits [n][d_out] in y_dtype
  *   ids     [n]        adapter id per token (negative: no adapter)
  *   A[a]    [r_a][d_in]   B[a] [d_out][r_a]   (stored bits, w_dtype), NULL if
  *                          that adapter is not supplied
+ *   a_scale[a] [r_a], b_scale[a] [r_a]: scales of a quantised adapter (NULL
+ *                          table or NULL entry: none, i.e. 1)
  *   ranks/scales [n_adapters]
  *   y_out   [n][d_out] double      v_out (optional) [n][v_ld] double, zero past r
  * Returns 0, -1 if a token names an adapter with no supplied weights, -2 on
  * bad arguments.
  */
-int oracle_lora_apply(int64_t n, int32_t d_in, int32_t d_out, int32_t w_dtype,
+int oracle_lora_apply(int64_t n, int32_t d_in, int32_t d_out, int32_t w_dtype, int32_t x_dtype,
                       int32_t y_dtype, const void* x_bits, const int32_t* ids,
                       int32_t n_adapters, const int32_t* ranks, const float* scales,
-                      const void* const* A, const void* const* B, const void* y0_bits,
-                      double* y_out, double* v_out, int32_t v_ld, int32_t n_threads) {
-  if (n < 0 || d_in <= 0 || d_out <= 0 || w_dtype < 0 || w_dtype > 2 || y_dtype < 0 ||
-      y_dtype > 2)
+                      const void* const* A, const void* const* B,
+                      const float* const* a_scale, const float* const* b_scale,
+                      const void* y0_bits, double* y_out, double* v_out, int32_t v_ld,
+                      int32_t n_threads) {
+  if (n < 0 || d_in <= 0 || d_out <= 0 || w_dtype < 0 || w_dtype > 3 || x_dtype < 0 ||
+      x_dtype > 2 || y_dtype < 0 || y_dtype > 2)
     return -2;
   for (int64_t i = 0; i < n; ++i) {
     int32_t a = ids[i];
@@ -163,21 +184,25 @@ int oracle_lora_apply(int64_t n, int32_t d_in, int32_t d_out, int32_t w_dtype,
     if (a < 0) continue;
     const int32_t r = ranks[a];
     const double s = (double)scales[a];
+    const float* sa = a_scale ? a_scale[a] : NULL;
+    const float* sb = b_scale ? b_scale[a] : NULL;
     double* v = (double*)malloc(sizeof(double) * (size_t)r);
     if (!v) { bad |= 1; continue; }
     /* shrink: v_k = sum_j A[k][j] x[j] */
     for (int32_t k = 0; k < r; ++k) {
+      const double ak = sa ? (double)sa[k] : 1.0;
       double acc = 0.0;
       for (int32_t j = 0; j < d_in; ++j)
-        acc += dec_at(A[a], w_dtype, (int64_t)k * d_in + j) *
-               dec_at(x_bits, w_dtype, i * (int64_t)d_in + j);
+        acc += (ak * dec_at(A[a], w_dtype, (int64_t)k * d_in + j)) *
+               dec_at(x_bits, x_dtype, i * (int64_t)d_in + j);
       v[k] = acc;
       if (v_out) v_out[i * (int64_t)v_ld + k] = acc;
     }
     /* expand: y[m] = y0[m] + s * sum_k B[m][k] v_k */
     for (int32_t m = 0; m < d_out; ++m) {
       double acc = 0.0;
-      for (int32_t k = 0; k < r; ++k) acc += dec_at(B[a], w_dtype, (int64_t)m * r + k) * v[k];
+      for (int32_t k = 0; k < r; ++k)
+        acc += (dec_at(B[a], w_dtype, (int64_t)m * r + k) * (sb ? (double)sb[k] : 1.0)) * v[k];
       yi[m] = yi[m] + s * acc;
     }
     free(v);
@@ -199,7 +224,7 @@ int oracle_lora_apply(int64_t n, int32_t d_in, int32_t d_out, int32_t w_dtype,
 int oracle_walk_adapter(const void* pool, int32_t dt, int32_t P, int64_t n_pages,
                         int32_t d_in, int32_t d_out, int32_t rank, const int32_t* a_pages,
                         const int32_t* b_pages, void* A_out, void* B_out) {
-  if (dt < 0 || dt > 2 || P <= 0 || rank <= 0) return -2;
+  if (dt < 0 || dt > 3 || P <= 0 || rank <= 0) return -2;
   const int es = elt_size(dt);
   const int per16 = 16 / es;
   const int32_t rs = (rank + per16 - 1) / per16 * per16;

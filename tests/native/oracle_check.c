@@ -10,11 +10,12 @@
 
 int oracle_round(const double* in, int64_t n, int32_t dt, void* out);
 int oracle_decode(const void* in, int64_t n, int32_t dt, double* out);
-int oracle_lora_apply(int64_t n, int32_t d_in, int32_t d_out, int32_t w_dtype, int32_t y_dtype,
-                      const void* x_bits, const int32_t* ids, int32_t n_adapters,
+int oracle_lora_apply(int64_t n, int32_t d_in, int32_t d_out, int32_t w_dtype, int32_t x_dtype,
+                      int32_t y_dtype, const void* x_bits, const int32_t* ids, int32_t n_adapters,
                       const int32_t* ranks, const float* scales, const void* const* A,
-                      const void* const* B, const void* y0_bits, double* y_out, double* v_out,
-                      int32_t v_ld, int32_t n_threads);
+                      const void* const* B, const float* const* a_scale,
+                      const float* const* b_scale, const void* y0_bits, double* y_out,
+                      double* v_out, int32_t v_ld, int32_t n_threads);
 int oracle_walk_adapter(const void* pool, int32_t dt, int32_t P, int64_t n_pages, int32_t d_in,
                         int32_t d_out, int32_t rank, const int32_t* a_pages,
                         const int32_t* b_pages, void* A_out, void* B_out);
@@ -60,13 +61,13 @@ int main(void) {
     void* y0 = rand_bits(ydt, (int64_t)n * d_out);
     double* y = malloc(sizeof(double) * (size_t)(n * d_out + 1));
     double* v = malloc(sizeof(double) * (size_t)(n * vld + 1));
-    CHECK(oracle_lora_apply(n, d_in, d_out, dt, ydt, x, ids, na, ranks, scales, A, B, y0, y, v, vld,
+    CHECK(oracle_lora_apply(n, d_in, d_out, dt, dt, ydt, x, ids, na, ranks, scales, A, B, NULL, NULL, y0, y, v, vld,
                             1 + (int)(rnd() % 3)) == 0);
-    CHECK(oracle_lora_apply(n, d_in, d_out, dt, ydt, x, ids, na, ranks, scales, A, B, y0, y, NULL, 0,
+    CHECK(oracle_lora_apply(n, d_in, d_out, dt, dt, ydt, x, ids, na, ranks, scales, A, B, NULL, NULL, y0, y, NULL, 0,
                             1) == 0);
     if (n > 0 && vld > 1)
-      CHECK(oracle_lora_apply(n, d_in, d_out, dt, ydt, x, ids, na, ranks, scales, A, B, y0, y, v,
-                              0, 1) != 0 || ids[0] < 0);
+      CHECK(oracle_lora_apply(n, d_in, d_out, dt, dt, ydt, x, ids, na, ranks, scales, A, B, NULL, NULL,
+                              y0, y, v, 0, 1) != 0 || ids[0] < 0);
     void* rb = malloc((size_t)(n * d_out + 1) * 4);
     CHECK(oracle_round(y, (int64_t)n * d_out, ydt, rb) == 0);
     double* back = malloc(sizeof(double) * (size_t)(n * d_out + 1));
@@ -75,11 +76,11 @@ int main(void) {
     if (n > 0) {
       const void* Anull[5] = {0};
       ids[0] = 0;
-      CHECK(oracle_lora_apply(n, d_in, d_out, dt, ydt, x, ids, na, ranks, scales, Anull, B, y0, y,
-                              NULL, 0, 1) == -1);
+      CHECK(oracle_lora_apply(n, d_in, d_out, dt, dt, ydt, x, ids, na, ranks, scales, Anull, B, NULL,
+                              NULL, y0, y, NULL, 0, 1) == -1);
     }
-    CHECK(oracle_lora_apply(n, 0, d_out, dt, ydt, x, ids, na, ranks, scales, A, B, y0, y, NULL, 0,
-                            1) == -2);
+    CHECK(oracle_lora_apply(n, 0, d_out, dt, dt, ydt, x, ids, na, ranks, scales, A, B, NULL, NULL, y0,
+                            y, NULL, 0, 1) == -2);
     for (int a = 0; a < na; ++a) {
       free((void*)A[a]);
       free((void*)B[a]);

@@ -293,3 +293,121 @@ def test_walker_reads_documented_layout(dtype, rank, P, d_in, d_out):
         pool[b_pages[0] * P + rank] = 1
         with pytest.raises(ValueError):
             oracle.walk_adapter(pool, dtype, P, d_in, d_out, rank, a_pages, b_pages)
+
+
+# --- quantised adapters: OCP FP8 E4M3 codes with per-row / per-column scales ----
+# Values of the format's defining codes (sign, 4 exponent bits with bias 7, 3
+# mantissa bits; subnormals m * 2^-9; no infinities; S.1111.111 is NaN).
+E4M3_ANCHORS = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2 ** -6,
+                0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+                0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+
+
+def test_e4m3_decoder_against_torch_and_the_format():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(codes, "e4m3")
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    assert int(np.isnan(got).sum()) == 2 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    for c, v in E4M3_ANCHORS.items():
+        assert got[c] == v and np.signbit(got[c]) == np.signbit(v), hex(c)
+    # monotone over the positive finite codes, symmetric in the sign bit
+    pos = got[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    np.testing.assert_array_equal(got[0x80:0xFF], -got[:0x7F])
+
+
+def _quant_dense(wl, a, s=0):
+    """Dequantised A, B of a quantised adapter, decoded by torch (independent of
+    the oracle) and scaled with numpy."""
+    torch = pytest.importorskip("torch")
+    A, B = wl.weights(a, s)
+    sa, sb = wl.qscales(a, s)
+    dec = lambda c: torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).double().numpy()
+    return sa.astype(np.float64)[:, None] * dec(A), dec(B) * sb.astype(np.float64)[None, :]
+
+
+def test_quantised_one_adapter_equals_two_gemms():
+    # P3 for quantised adapters: y0 + s (X A^T) B^T with A = diag(sa) A_q, B = B_q diag(sb)
+    wl = W.small_workload("e4m3", 96, 80, [7], 96, act_dtype="bf16")
+    b = W.custom_batch(wl, [0] * 11)
+    y = oracle.workload_reference(wl, b, 0)
+    A, B = _quant_dense(wl, 0)
+    X = W.dequantize(b.x[0], "bf16")
+    Y0 = W.dequantize(b.y0[0], "bf16")
+    ref = Y0 + float(wl.scales[0]) * ((X @ A.T) @ B.T)
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+    # dropping either scale set, or applying the row scales of A to B, fails
+    sa, sb = wl.qscales(0, 0)
+    Aq, Bq = A / sa[:, None], B / sb[None, :]
+    for wrong in ((Aq, B), (A, Bq), (A, Bq * sa[None, :])):
+        bad = Y0 + float(wl.scales[0]) * ((X @ wrong[0].T) @ wrong[1].T)
+        assert np.abs(y - bad).max() > 1e-3 * np.abs(ref - Y0).max()
+
+
+def test_quantised_rank1_closed_form():
+    # y_i = y0_i + s * sa * sb * (a_q . x_i) * b_q, exactly
+    rng = np.random.default_rng(21)
+    d_in, d_out, n = 40, 24, 7
+    aq = rng.integers(-3, 4, size=d_in).astype(np.float64)
+    bq = rng.integers(-3, 4, size=d_out).astype(np.float64)
+    A = W.quantize_e4m3(aq)[None, :]
+    B = W.quantize_e4m3(bq)[:, None]
+    X = rng.integers(-5, 6, size=(n, d_in)).astype(np.float32)
+    Y0 = rng.integers(-5, 6, size=(n, d_out)).astype(np.float32)
+    sa, sb, s = np.float32(0.375), np.float32(1.25), np.float32(0.5)
+    y = oracle.lora_apply(X, np.zeros(n, np.int32), np.array([1], np.int32), np.array([s]),
+                          {0: (A, B, np.array([sa]), np.array([sb]))}, Y0, "e4m3", "f32",
+                          x_dtype="f32")
+    for i in range(n):
+        dot = sum(int(aq[j]) * int(X[i, j]) for j in range(d_in))
+        k = Fraction(float(s)) * Fraction(float(sa)) * Fraction(float(sb)) * dot
+        want = [Fraction(int(Y0[i, m])) + k * int(bq[m]) for m in range(d_out)]
+        assert [Fraction(v) for v in y[i]] == want
+
+
+def test_quantised_exact_integer_mode():
+    wl = W.small_workload("e4m3", 128, 72, [8, 5, 16, 1], 128, exact=True, act_dtype="f16")
+    b = W.custom_batch(wl, [3, 0, 2, 2, -1, 1, 0, 3])
+    y, v = oracle.workload_reference(wl, b, 0, return_v=True)
+    X = W.dequantize(b.x[0], "f16")
+    Y0 = W.dequantize(b.y0[0], "f16")
+    for i, a in enumerate(b.ids.tolist()):
+        if a < 0:
+            np.testing.assert_array_equal(y[i], Y0[i])
+            continue
+        A, B = _quant_dense(wl, a)
+        vi = [sum(Fraction(A[k, j]) * Fraction(X[i, j]) for j in range(128)) for k in range(A.shape[0])]
+        assert [Fraction(t) for t in v[i, :A.shape[0]]] == vi
+        want = [Fraction(Y0[i, m]) + Fraction(float(wl.scales[a])) *
+                sum(Fraction(B[m, k]) * vi[k] for k in range(A.shape[0])) for m in range(72)]
+        assert [Fraction(t) for t in y[i]] == want
+
+
+def test_walker_reads_e4m3_layout():
+    # one-byte elements: r_s = rank rounded up to 16, floor(P / r_s) B rows per page
+    rng = np.random.default_rng(6)
+    rank, P, d_in, d_out = 5, 64, 100, 30
+    rs, npa = 16, -(-100 // 64)
+    rpp = P // rs
+    npb = -(-d_out // rpp)
+    n_pages = rank * npa + npb + 5
+    pages = rng.permutation(n_pages)[: rank * npa + npb].astype(np.int32)
+    a_pages, b_pages = pages[: rank * npa], pages[rank * npa:]
+    pool = np.full(n_pages * P, 0x7F, np.uint8)
+    A = rng.integers(1, 0x7E, size=(rank, d_in)).astype(np.uint8)
+    B = rng.integers(1, 0x7E, size=(d_out, rank)).astype(np.uint8)
+    for k in range(rank):
+        for j in range(d_in):
+            pool[a_pages[k * npa + j // P] * P + j % P] = A[k, j]
+    for m in range(d_out):
+        base = b_pages[m // rpp] * P + (m % rpp) * rs
+        pool[base: base + rs] = 0
+        pool[base: base + rank] = B[m]
+    A2, B2 = oracle.walk_adapter(pool, "e4m3", P, d_in, d_out, rank, a_pages, b_pages)
+    np.testing.assert_array_equal(A2, A)
+    np.testing.assert_array_equal(B2, B)

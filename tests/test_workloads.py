@@ -80,3 +80,33 @@ def test_exact_mode_values():
     A, B = wl.weights(1, 0)
     assert set(np.unique(W.dequantize(A, "bf16")).tolist()) <= {-1.0, 0.0, 1.0}
     assert all(float(s) == 2.0 ** -np.floor(np.log2(r)) for s, r in zip(wl.scales, wl.ranks))
+
+
+def test_e4m3_generator_matches_torch_conversion():
+    # the input quantiser (RNE, saturating) and decoder of the generators agree
+    # with torch's float8_e4m3fn conversions
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.normal(0, 100, 100000), rng.normal(0, 0.01, 10000),
+                        [448.0, 449.0, 464.0, 1e9, -1e9, 0.0, 2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -9]])
+    q = W.quantize_e4m3(x)
+    qt = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(q, qt)
+    codes = np.arange(256, dtype=np.uint8)
+    d = W.dequantize(codes, "e4m3")
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(np.isnan(d), np.isnan(ref))
+    np.testing.assert_array_equal(d[~np.isnan(d)], ref[~np.isnan(ref)])
+
+
+def test_quantised_workload_shapes():
+    wl = W.make_workload(5)
+    assert wl.dtype == "e4m3" and wl.act_dtype == "f16" and wl.quantized
+    A, B = wl.weights(3, 1)
+    sa, sb = wl.qscales(3, 1)
+    assert A.dtype == np.uint8 and A.shape == (16, 4096) and B.shape == (4096, 16)
+    assert sa.dtype == np.float32 and sa.shape == (16,) and sb.shape == (16,)
+    w = sa[:, None].astype(np.float64) * W.dequantize(A, "e4m3")
+    assert 0.012 < w.std() < 0.03 and np.all(np.isfinite(w))
+    b = W.make_batch(wl, 0)
+    assert b.x[0].dtype == np.uint16 and len(b.ids) == 64

@@ -24,11 +24,11 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-DTYPES = ("f32", "f16", "bf16")
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
-ELT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+DTYPES = ("f32", "f16", "bf16", "e4m3")
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
+ELT_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
 # quiet-NaN bit patterns used to poison unused pool memory
-NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "e4m3": 0x7F}
 
 
 # ----------------------------------------------------------------------------
@@ -49,8 +49,36 @@ def quantize(a: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def quantize_e4m3(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to OCP FP8 E4M3 codes (uint8), nearest even, with
+    magnitudes past the largest finite value (448) saturated to it.  E4M3: sign,
+    4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+    subnormals m * 2^-9."""
+    a = np.asarray(a, dtype=np.float64)
+    sign = np.signbit(a)
+    x = np.minimum(np.abs(a), 448.0)
+    _, ex = np.frexp(x)                       # x = f * 2^ex, 0.5 <= f < 1
+    e = np.clip(ex - 1, -6, 8)                # binade exponent, subnormals share -6
+    quantum = np.ldexp(1.0, e - 3)
+    r = np.minimum(np.round(x / quantum) * quantum, 448.0)   # np.round: ties to even
+    _, rex = np.frexp(r)
+    re_ = rex - 1
+    normal = (r >= 2.0 ** -6)
+    mant = np.where(normal, np.round(np.ldexp(r, -re_) * 8) - 8, np.round(np.ldexp(r, 9)))
+    code = np.where(normal, ((re_ + 7) << 3) + mant, mant).astype(np.int64)
+    code = np.where(r == 0, 0, code)
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
 def dequantize(bits: np.ndarray, dtype: str) -> np.ndarray:
     """Stored form -> float64 (exact).  Used by tests and generators only."""
+    if dtype == "e4m3":
+        b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+        e, m = (b >> 3) & 15, b & 7
+        v = np.where(e == 0, np.ldexp(m.astype(np.float64), -9),
+                     np.ldexp((8 + m).astype(np.float64), (e - 10).astype(np.int64)))
+        v = np.where((e == 15) & (m == 7), np.nan, v)
+        return np.where(b >> 7, -v, v)
     if dtype == "f32":
         return np.asarray(bits, dtype=np.float32).astype(np.float64)
     if dtype == "f16":
@@ -62,7 +90,7 @@ def dequantize(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def storage_np_dtype(dtype: str):
-    return np.float32 if dtype == "f32" else np.uint16
+    return {"f32": np.float32, "e4m3": np.uint8}.get(dtype, np.uint16)
 
 
 # ----------------------------------------------------------------------------
@@ -130,6 +158,33 @@ class Workload:
     bank: Optional[np.ndarray] = None      # stored-bits weight bank (large configs)
     _bank_offsets: Optional[np.ndarray] = None
     _dense_cache: Dict = dataclasses.field(default_factory=dict)
+    act_dtype: Optional[str] = None        # x (and 16-bit y) dtype; default: dtype
+
+    def __post_init__(self):
+        if self.act_dtype is None:
+            self.act_dtype = self.dtype
+
+    @property
+    def quantized(self) -> bool:
+        return self.dtype == "e4m3"
+
+    def qscales(self, adapter: int, slice_idx: int):
+        """Scales of a quantised adapter slice: (a_scale [r] per rank row of A,
+        b_scale [r] per rank column of B), float32; None for other dtypes.
+        Drawn per (adapter, slice): 0.02/64 * 2^U(-1/2, 1/2) (codes come from
+        N(0, 1) * 64, so the weights are ~N(0, 0.02)); exact mode: powers of
+        two in {1/2, 1, 2}."""
+        if not self.quantized:
+            return None
+        r = int(self.ranks[adapter])
+        rng = np.random.Generator(np.random.PCG64([self.seed, 7321, slice_idx, adapter]))
+        if self.exact:
+            sa = 2.0 ** rng.integers(-1, 2, size=r)
+            sb = 2.0 ** rng.integers(-1, 2, size=r)
+        else:
+            sa = 0.02 / 64 * 2.0 ** rng.uniform(-0.5, 0.5, size=r)
+            sb = 0.02 / 64 * 2.0 ** rng.uniform(-0.5, 0.5, size=r)
+        return sa.astype(np.float32), sb.astype(np.float32)
 
     @property
     def n_adapters(self) -> int:
@@ -156,8 +211,11 @@ class Workload:
             rng = np.random.Generator(np.random.PCG64(
                 [self.seed, 7919, slice_idx, adapter]))
             if self.exact:
-                A = quantize(rng.integers(-1, 2, size=(r, d_in)), self.dtype)
-                B = quantize(rng.integers(-1, 2, size=(d_out, r)), self.dtype)
+                A = _store(rng.integers(-1, 2, size=(r, d_in)), self.dtype)
+                B = _store(rng.integers(-1, 2, size=(d_out, r)), self.dtype)
+            elif self.quantized:
+                A = quantize_e4m3(rng.normal(0.0, 1.0, size=(r, d_in)) * 64)
+                B = quantize_e4m3(rng.normal(0.0, 1.0, size=(d_out, r)) * 64)
             else:
                 A = quantize(rng.normal(0.0, 0.02, size=(r, d_in)), self.dtype)
                 B = quantize(rng.normal(0.0, 0.02, size=(d_out, r)), self.dtype)
@@ -195,13 +253,20 @@ CONFIG_NAMES = {
     2: "hetero_decode_bgmv",
     3: "llama13b_prefill_sgmv",
     4: "llama70b_mixed_apply",
+    # the Llama-7B decode batch with FP8 E4M3 adapter pages (per-row scales)
+    5: "llama7b_decode_bgmv_fp8",
 }
+
+
+def _store(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored form of float64 draws: RNE to the dtype (E4M3 codes for e4m3)."""
+    return quantize_e4m3(a) if dtype == "e4m3" else quantize(a, dtype)
 
 
 def _ranks_and_scales(cfg: int, rng, exact: bool, alpha: float = 16.0):
     if cfg == 0:
         ranks = np.array([4, 8, 8, 16], np.int32)
-    elif cfg == 1:
+    elif cfg in (1, 5):
         ranks = np.full(1000, 16, np.int32)
     elif cfg == 2:
         ranks = rng.choice(np.array([8, 16, 32, 64], np.int32), size=2000)
@@ -244,11 +309,15 @@ def make_workload(cfg: int, exact: bool = False, seed: Optional[int] = None,
                       [(5120, 5120), (5120, 13824)], ranks, scales, seed,
                       shuffle_seed=seed * 31 + 7, pool_slack=1.25, kv_dummy_ratio=0.0,
                       exact=exact)
-    else:
+    elif cfg == 4:
         wl = Workload("llama70b_mixed_apply", "mixed", "bf16", 8192,
                       [(8192, 8192), (8192, 28672)], ranks, scales, seed,
                       shuffle_seed=seed * 31 + 7, pool_slack=1.05, kv_dummy_ratio=0.0,
                       exact=exact)
+    else:
+        wl = Workload("llama7b_decode_bgmv_fp8", "bgmv", "e4m3", 4096, [(4096, 4096)] * 4,
+                      ranks, scales, seed, shuffle_seed=seed * 31 + 7, pool_slack=1.25,
+                      kv_dummy_ratio=0.0, exact=exact, act_dtype="f16")
     # Large populations draw every adapter slice as a window of one iid weight
     # bank at a seeded offset: each window is iid N(0, 0.02) (or {-1,0,1}), and
     # generating thousands of adapters costs one bank instead of one draw each.
@@ -257,7 +326,9 @@ def make_workload(cfg: int, exact: bool = False, seed: Optional[int] = None,
         n_bank = bank_elems or max(1 << 24, 4 * need)
         brng = np.random.Generator(np.random.PCG64([seed, 2]))
         if exact:
-            wl.bank = quantize(brng.integers(-1, 2, size=n_bank), wl.dtype)
+            wl.bank = _store(brng.integers(-1, 2, size=n_bank), wl.dtype)
+        elif wl.quantized:
+            wl.bank = quantize_e4m3(brng.normal(0.0, 1.0, size=n_bank) * 64)
         else:
             wl.bank = quantize(brng.normal(0.0, 0.02, size=n_bank), wl.dtype)
         orng = np.random.Generator(np.random.PCG64([seed, 3]))
@@ -288,7 +359,7 @@ def make_batch(wl: Workload, index: int = 0, y_dtype: Optional[str] = None,
                slices: Optional[Sequence[int]] = None, with_x: bool = True) -> Batch:
     """Draw batch `index` of the workload: ids (+ segment layout) and, per slice,
     x and y0.  `n_tokens` overrides the token count of BGMV configurations."""
-    y_dtype = y_dtype or wl.dtype
+    y_dtype = y_dtype or wl.act_dtype
     rng = np.random.Generator(np.random.PCG64([wl.seed, 100 + index]))
     N = wl.n_adapters
     seg = None
@@ -297,7 +368,7 @@ def make_batch(wl: Workload, index: int = 0, y_dtype: Optional[str] = None,
     if wl.name == "tiny_bgmv":
         n = n_tokens or 8
         ids = rng.integers(0, N, size=n).astype(np.int32)
-    elif wl.name == "llama7b_decode_bgmv":
+    elif wl.name in ("llama7b_decode_bgmv", "llama7b_decode_bgmv_fp8"):
         n = n_tokens or 64
         ids = rng.integers(0, N, size=n).astype(np.int32)
     elif wl.name == "hetero_decode_bgmv":
@@ -335,7 +406,7 @@ def make_batch(wl: Workload, index: int = 0, y_dtype: Optional[str] = None,
             continue
         d_in, d_out = wl.slices[s]
         srng = np.random.Generator(np.random.PCG64([wl.seed, 200 + index, s]))
-        xs.append(_activations(srng, n, d_in, wl.dtype, wl.exact))
+        xs.append(_activations(srng, n, d_in, wl.act_dtype, wl.exact))
         y0s.append(_y0(srng, n, d_out, y_dtype, wl.exact, zero_y0))
     return Batch(ids=ids, x=xs, y0=y0s, seg_lengths=seg, n_decode=n_dec)
 
@@ -343,7 +414,8 @@ def make_batch(wl: Workload, index: int = 0, y_dtype: Optional[str] = None,
 def small_workload(dtype: str, d_in: int, d_out: int, ranks: Sequence[int], page_elems: int,
                    seed: int = 5, exact: bool = False, alpha: float = 16.0,
                    scales: Optional[Sequence[float]] = None, n_slices: int = 1,
-                   pool_slack: float = 2.0, kv_dummy_ratio: float = 0.0) -> Workload:
+                   pool_slack: float = 2.0, kv_dummy_ratio: float = 0.0,
+                   act_dtype: Optional[str] = None) -> Workload:
     """An ad-hoc population for edge-case tests (odd ranks, ragged pages, ...)."""
     ranks = np.asarray(ranks, np.int32)
     if scales is None:
@@ -351,19 +423,22 @@ def small_workload(dtype: str, d_in: int, d_out: int, ranks: Sequence[int], page
             scales = [2.0 ** -math.floor(math.log2(r)) for r in ranks]
         else:
             scales = [alpha / float(r) for r in ranks]
+    if act_dtype is None and dtype == "e4m3":
+        act_dtype = "bf16"
     return Workload("custom", "bgmv", dtype, page_elems, [(d_in, d_out)] * n_slices, ranks,
                     np.asarray(scales, np.float32), seed, shuffle_seed=seed * 31 + 7,
-                    pool_slack=pool_slack, kv_dummy_ratio=kv_dummy_ratio, exact=exact)
+                    pool_slack=pool_slack, kv_dummy_ratio=kv_dummy_ratio, exact=exact,
+                    act_dtype=act_dtype)
 
 
 def custom_batch(wl: Workload, ids: Sequence[int], index: int = 0, y_dtype: Optional[str] = None,
                  zero_y0: bool = False) -> Batch:
-    y_dtype = y_dtype or wl.dtype
+    y_dtype = y_dtype or wl.act_dtype
     ids = np.asarray(ids, np.int32)
     n = ids.shape[0]
     xs, y0s = [], []
     for s, (d_in, d_out) in enumerate(wl.slices):
         srng = np.random.Generator(np.random.PCG64([wl.seed, 300 + index, s]))
-        xs.append(_activations(srng, n, d_in, wl.dtype, wl.exact))
+        xs.append(_activations(srng, n, d_in, wl.act_dtype, wl.exact))
         y0s.append(_y0(srng, n, d_out, y_dtype, wl.exact, zero_y0))
     return Batch(ids=ids, x=xs, y0=y0s)
