@@ -35,7 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "BGMV/SGMV tokens/s and achieved HBM GB/s (% of peak), Llama-7B/70B shapes, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 WORKLOADS = {"llama7b_decode_bgmv": 1, "hetero_decode_bgmv": 2, "llama13b_prefill_sgmv": 3,
-             "llama70b_mixed_apply": 4}
+             "llama70b_mixed_apply": 4, "llama7b_decode_bgmv_fp8": 5}
+ELT = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
 CSRC = os.path.join(ROOT, "gather_lora_matmul_amd", "csrc")
 # Sources each path's kernels are compiled from (traffic figures taken on other
 # code are dropped).
@@ -46,16 +47,18 @@ PLANNED_SOURCES = ("k_sgmv.hip", "kmfma.h", "kcommon.h", "kvalu.h", "lora_intern
 
 def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int) -> int:
     """Bytes the method must move for one step: each distinct adapter's A and B
-    once per slice, x once, y read and written once."""
-    elt = 4 if wl.dtype == "f32" else 2
+    once per slice (FP8 pages: one byte per code plus the 2 r fp32 scales), x
+    once, y read and written once."""
+    elt, elt_x = ELT[wl.dtype], ELT[wl.act_dtype]
     total = 0
     uniq = sorted(set(int(a) for a in ids.tolist() if a >= 0))
     n = len(ids)
     for s in slices:
         d_in, d_out = wl.slices[s]
         for a in uniq:
-            total += int(wl.ranks[a]) * (d_in + d_out) * elt
-        total += n * d_in * elt + 2 * n * d_out * elt_y
+            r = int(wl.ranks[a])
+            total += r * (d_in + d_out) * elt + (8 * r if wl.quantized else 0)
+        total += n * d_in * elt_x + 2 * n * d_out * elt_y
     return total
 
 
@@ -143,7 +146,7 @@ class Runner:
         self.L, self.torch = L, torch
         cfg = WORKLOADS[name]
         self.wl = wl = W.make_workload(cfg)
-        self.planned = planned or cfg >= 3
+        self.planned = planned or cfg in (3, 4)
         self.mode = mode
         self.slices = slices = list(range(len(wl.slices)))
         n_batches = n_batches or (4 if self.planned else 16)
@@ -154,9 +157,9 @@ class Runner:
         self.setup_s = time.perf_counter() - t0
         self.batches = [W.make_batch(wl, i) for i in range(n_batches)]
         self.ids_d = [torch.from_numpy(b.ids).cuda() for b in self.batches]
-        self.xs = [[to_device(b.x[s], wl.dtype) for s in slices] for b in self.batches]
-        self.ys = [[to_device(b.y0[s], wl.dtype) for s in slices] for b in self.batches]
-        self.ydt = W.DTYPE_CODE[wl.dtype]
+        self.xs = [[to_device(b.x[s], wl.act_dtype) for s in slices] for b in self.batches]
+        self.ys = [[to_device(b.y0[s], wl.act_dtype) for s in slices] for b in self.batches]
+        self.ydt = W.DTYPE_CODE[wl.act_dtype]
         self.n = len(self.batches[0].ids)
         self.v = [torch.zeros((self.n, self.sp.max_rank), dtype=torch.float32, device="cuda")
                   for _ in slices]
@@ -336,7 +339,7 @@ def main():
         "config": {"workload": wl.name, "tokens_per_step": head.n,
                    "slices": ", ".join("%dx%d" % tuple(d) for d in wl.slices),
                    "adapters": wl.n_adapters,
-                   "rank": sorted(set(int(r) for r in wl.ranks)) if cfg != 1 else 16,
+                   "rank": sorted(set(int(r) for r in wl.ranks)) if cfg not in (1, 5) else 16,
                    "weights": "%s N(0,0.02), pages scattered" % wl.dtype,
                    "entry": head.entry, "id_batches_rotated": len(head.batches)},
         "roofline": rec["roofline"],
@@ -360,9 +363,10 @@ def main():
         extra = {}
         steps = min(args.steps, 50)
         warm = min(args.warmup, 5)
-        for name, planned in (("hetero_decode_bgmv", False), ("hetero_decode_bgmv", True),
-                              ("llama13b_prefill_sgmv", True), ("llama70b_mixed_apply", True)):
-            key = name + ("/planned" if planned and WORKLOADS[name] < 3 else "")
+        for name, planned in (("llama7b_decode_bgmv_fp8", False), ("hetero_decode_bgmv", False),
+                              ("hetero_decode_bgmv", True), ("llama13b_prefill_sgmv", True),
+                              ("llama70b_mixed_apply", True)):
+            key = name + ("/planned" if planned and WORKLOADS[name] in (1, 2) else "")
             if name == args.workload and planned == head.planned:
                 continue
             r = Runner(name, "fused", planned)

@@ -17,8 +17,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
 
-LORA_F32, LORA_F16, LORA_BF16 = 0, 1, 2
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+LORA_F32, LORA_F16, LORA_BF16, LORA_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
 LORA_OK = 0
 STATUS = {0: "LORA_OK", -1: "LORA_E_ARG", -2: "LORA_E_NOMEM", -3: "LORA_E_NOT_RESIDENT",
           -4: "LORA_E_RANK", -5: "LORA_E_STATE", -6: "LORA_E_HIP", -7: "LORA_E_UNSUPPORTED"}
@@ -31,12 +31,13 @@ LORA_MAX_IO = 8
 # Every symbol the header declares.
 EXPORTS = (
     "lora_pool_create", "lora_pool_destroy", "lora_pool_info", "lora_pool_alloc_pages",
-    "lora_pool_free_pages", "lora_pool_upload", "lora_pool_evict", "lora_page_table_build",
-    "lora_pool_export_entry", "lora_pool_read_pages", "lora_bgmv_shrink", "lora_bgmv_expand",
+    "lora_pool_free_pages", "lora_pool_upload", "lora_pool_upload_scaled", "lora_pool_evict",
+    "lora_page_table_build", "lora_pool_export_entry", "lora_pool_export_scales",
+    "lora_pool_read_pages", "lora_bgmv_shrink", "lora_bgmv_expand",
     "lora_bgmv_apply", "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
     "lora_plan_get_stats", "lora_plan_export", "lora_plan_prepare", "lora_workspace_size",
     "lora_sgmv_shrink", "lora_sgmv_expand", "lora_apply", "lora_apply_noalloc", "lora_debug_resolve",
-    "lora_debug_gather", "lora_last_error",
+    "lora_debug_gather", "lora_debug_decode", "lora_last_error",
 )
 
 
@@ -53,7 +54,7 @@ class PoolDesc(ctypes.Structure):
                 ("slice_d_in", ctypes.POINTER(ctypes.c_int32)),
                 ("slice_d_out", ctypes.POINTER(ctypes.c_int32)),
                 ("shuffle_seed", ctypes.c_uint64), ("flags", ctypes.c_uint32),
-                ("pages_dev", ctypes.c_void_p)]
+                ("pages_dev", ctypes.c_void_p), ("act_dtype", ctypes.c_int32)]
 
 
 class Io(ctypes.Structure):
@@ -87,6 +88,9 @@ def _load() -> ctypes.CDLL:
         "lora_pool_alloc_pages": [V, I64, V],
         "lora_pool_free_pages": [V, I64, V],
         "lora_pool_upload": [V, I32, I32, I32, F, V, V, V],
+        "lora_pool_upload_scaled": [V, I32, I32, I32, F, V, V, V, V, V],
+        "lora_pool_export_scales": [V, I32, I32, V, V],
+        "lora_debug_decode": [I32, V, I64, V, V],
         "lora_pool_evict": [V, I32, I32, V],
         "lora_page_table_build": [V, V],
         "lora_pool_export_entry": [V, I32, I32, V, V, V, V, V, V],
@@ -200,17 +204,19 @@ def _stream(stream) -> Optional[int]:
 # ----------------------------------------------------------------------------
 def lora_pool_create(page_elems: int, dtype: int, n_pages: int, max_adapters: int, max_rank: int,
                      slice_dims: Sequence[Tuple[int, int]], shuffle_seed: int = 0, flags: int = 0,
-                     pages_dev=None) -> int:
+                     pages_dev=None, act_dtype: Optional[int] = None) -> int:
     """Returns an opaque pool handle (int).  `pages_dev` may be a torch tensor
-    that provides the page memory (the caller keeps it alive)."""
+    that provides the page memory (the caller keeps it alive).  act_dtype: the
+    dtype of x (default: the page dtype; f16 or bf16 for FP8 pages)."""
     ns = len(slice_dims)
     din = (ctypes.c_int32 * ns)(*[int(a) for a, _ in slice_dims])
     dout = (ctypes.c_int32 * ns)(*[int(b) for _, b in slice_dims])
+    act = dtype if act_dtype is None else act_dtype
     d = PoolDesc(page_elems, dtype, n_pages, max_adapters, max_rank, ns, din, dout,
-                 shuffle_seed, flags, _dev_ptr(pages_dev) if pages_dev is not None else None)
+                 shuffle_seed, flags, _dev_ptr(pages_dev) if pages_dev is not None else None, act)
     h = ctypes.c_void_p()
     _check(_lib.lora_pool_create(ctypes.byref(d), ctypes.byref(h)), "lora_pool_create")
-    _POOLS[h.value] = (int(dtype), [(int(a), int(b)) for a, b in slice_dims], int(max_rank))
+    _POOLS[h.value] = (int(act), [(int(a), int(b)) for a, b in slice_dims], int(max_rank))
     return h.value
 
 
@@ -247,6 +253,30 @@ def lora_pool_upload(pool: int, adapter: int, slice_: int, rank: int, scale: flo
            "lora_pool_upload")
 
 
+def lora_pool_upload_scaled(pool: int, adapter: int, slice_: int, rank: int, scale: float,
+                            A_host: np.ndarray, a_scale: np.ndarray, B_host: np.ndarray,
+                            b_scale: np.ndarray, stream=None):
+    A = np.ascontiguousarray(A_host)
+    B = np.ascontiguousarray(B_host)
+    sa = np.ascontiguousarray(a_scale, np.float32)
+    sb = np.ascontiguousarray(b_scale, np.float32)
+    if sa.size < rank or sb.size < rank:
+        raise ValueError("scale arrays need rank entries")
+    _check(_lib.lora_pool_upload_scaled(pool, adapter, slice_, rank, float(scale), _np_ptr(A),
+                                        _np_ptr(sa), _np_ptr(B), _np_ptr(sb),
+                                        stream if isinstance(stream, int) else None),
+           "lora_pool_upload_scaled")
+
+
+def lora_pool_export_scales(pool: int, adapter: int, slice_: int, rank: int):
+    """-> (a_scale, b_scale) float32 [rank] of a quantised adapter slice."""
+    sa = np.empty(rank, np.float32)
+    sb = np.empty(rank, np.float32)
+    _check(_lib.lora_pool_export_scales(pool, adapter, slice_, _np_ptr(sa), _np_ptr(sb)),
+           "lora_pool_export_scales")
+    return sa, sb
+
+
 def lora_pool_evict(pool: int, adapter: int, slice_: int, stream=None):
     _check(_lib.lora_pool_evict(pool, adapter, slice_, stream if isinstance(stream, int) else None),
            "lora_pool_evict")
@@ -274,7 +304,7 @@ def lora_pool_export_entry(pool: int, adapter: int, slice_: int):
 
 
 def lora_pool_read_pages(pool: int, first: int, count: int, page_elems: int, dtype: int) -> np.ndarray:
-    out = np.empty(count * page_elems, np.float32 if dtype == LORA_F32 else np.uint16)
+    out = np.empty(count * page_elems, {LORA_F32: np.float32, LORA_FP8_E4M3: np.uint8}.get(dtype, np.uint16))
     _check(_lib.lora_pool_read_pages(pool, first, count, _np_ptr(out)), "lora_pool_read_pages")
     return out
 
@@ -494,6 +524,14 @@ def lora_debug_resolve(pool: int, slice_: int, ids, a_off, b_off, stream=None):
 def lora_debug_gather(pool: int, slice_: int, adapter: int, A, B, stream=None):
     _check(_lib.lora_debug_gather(pool, slice_, adapter, _dev_ptr(A), _dev_ptr(B), _stream(stream)),
            "lora_debug_gather")
+
+
+def lora_debug_decode(dtype: int, src, dst, stream=None):
+    """dst (float32) = the stored elements of src decoded by the kernels' decoder."""
+    n = src.numel() * src.element_size() // {LORA_F32: 4, LORA_FP8_E4M3: 1}.get(dtype, 2)
+    _check_tensor(dst, "dst", LORA_F32, n)
+    _check(_lib.lora_debug_decode(dtype, _dev_ptr(src), n, _dev_ptr(dst), _stream(stream)),
+           "lora_debug_decode")
 
 
 def lora_last_error() -> str:

@@ -27,8 +27,8 @@ lora_status check_slice(const lora_pool* p, int32_t slice) {
 }
 
 lora_status check_ydt(const lora_pool* p, int32_t y_dtype) {
-  if (y_dtype != p->dtype && y_dtype != LORA_F32)
-    return fail(LORA_E_ARG, "y dtype %d must be the pool dtype or LORA_F32", y_dtype);
+  if (y_dtype != p->act && y_dtype != LORA_F32)
+    return fail(LORA_E_ARG, "y dtype %d must be the activation dtype or LORA_F32", y_dtype);
   return LORA_OK;
 }
 
@@ -112,8 +112,8 @@ lora_status lora_bgmv_shrink(lora_pool* p, int32_t slice, const void* x, const i
   if (!x || !ids || !v) return fail(LORA_E_ARG, "null device pointer");
   if (!aligned16(x)) return fail(LORA_E_ARG, "x not 16-byte aligned");
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
-  return hip_status(launch_bgmv_shrink(p->dtype, p->view(), p->io(slice, x, nullptr), ids, n, v,
-                                       v_ld, (hipStream_t)stream),
+  return hip_status(launch_bgmv_shrink(p->types(p->act), p->view(), p->io(slice, x, nullptr), ids, n,
+                                       v, v_ld, (hipStream_t)stream),
                     "bgmv_shrink");
 }
 
@@ -129,7 +129,7 @@ lora_status lora_bgmv_expand(lora_pool* p, int32_t slice, const float* v, int32_
   if (!v || !ids || !y) return fail(LORA_E_ARG, "null device pointer");
   if (!aligned16(y)) return fail(LORA_E_ARG, "y not 16-byte aligned");
   if (v_ld < p->max_rank) return fail(LORA_E_ARG, "v_ld %d < max_rank %d", v_ld, p->max_rank);
-  return hip_status(launch_bgmv_expand(p->dtype, y_dtype, p->view(), p->io(slice, nullptr, y), v,
+  return hip_status(launch_bgmv_expand(p->types(y_dtype), p->view(), p->io(slice, nullptr, y), v,
                                        v_ld, ids, n, tok_scale, (hipStream_t)stream),
                     "bgmv_expand");
 }
@@ -144,7 +144,7 @@ lora_status lora_bgmv_apply(lora_pool* p, int32_t n_io, const lora_io* io, const
   if (n < 0) return fail(LORA_E_ARG, "n < 0");
   if (n == 0) return LORA_OK;
   if (!ids) return fail(LORA_E_ARG, "null ids");
-  return hip_status(launch_bgmv_apply(p->dtype, y_dtype, p->view(), ios, ids, n, (hipStream_t)stream),
+  return hip_status(launch_bgmv_apply(p->types(y_dtype), p->view(), ios, ids, n, (hipStream_t)stream),
                     "bgmv_apply");
 }
 
@@ -162,7 +162,7 @@ lora_status lora_sgmv_shrink(lora_pool* p, const lora_plan* pl, int32_t slice, c
   const PlanLayout* lay = nullptr;
   LORA_TRY(find_layout(pl, single_io(io), ws, ws_bytes, true, &lay));
   LORA_TRY(check_pool(p));
-  return hip_status(launch_sgmv_shrink(p->dtype, p->view(), pl->view(lay, ws), io, v, v_ld,
+  return hip_status(launch_sgmv_shrink(p->types(p->act), p->view(), pl->view(lay, ws), io, v, v_ld,
                                        (hipStream_t)stream),
                     "sgmv_shrink");
 }
@@ -181,7 +181,7 @@ lora_status lora_sgmv_expand(lora_pool* p, const lora_plan* pl, int32_t slice, c
   const IoDesc io = p->io(slice, nullptr, y);
   const PlanLayout* lay = nullptr;
   LORA_TRY(find_layout(pl, single_io(io), nullptr, 0, false, &lay));
-  return hip_status(launch_sgmv_expand(p->dtype, y_dtype, p->view(), pl->view(lay, nullptr), io, v, v_ld,
+  return hip_status(launch_sgmv_expand(p->types(y_dtype), p->view(), pl->view(lay, nullptr), io, v, v_ld,
                                        (hipStream_t)stream),
                     "sgmv_expand");
 }
@@ -198,7 +198,7 @@ lora_status lora_apply(lora_pool* p, const lora_plan* pl, int32_t n_io, const lo
   const PlanLayout* lay = nullptr;
   LORA_TRY(find_layout(pl, ios, ws, ws_bytes, true, &lay));
   LORA_TRY(check_pool(p));
-  return hip_status(launch_apply(p->dtype, y_dtype, p->view(), pl->view(lay, ws), ios,
+  return hip_status(launch_apply(p->types(y_dtype), p->view(), pl->view(lay, ws), ios,
                                  (hipStream_t)stream),
                     "apply");
 }
@@ -228,6 +228,16 @@ lora_status lora_debug_gather(lora_pool* p, int32_t slice, int32_t adapter, void
   return hip_status(launch_debug_gather(p->elt, p->view(), p->io(slice, nullptr, nullptr), adapter,
                                         sl.rank, A, B, (hipStream_t)stream),
                     "debug_gather");
+}
+
+lora_status lora_debug_decode(int32_t dtype, const void* src, int64_t n, float* dst, void* stream) {
+  clear_error();
+  if (dtype < LORA_F32 || dtype > LORA_FP8_E4M3) return fail(LORA_E_ARG, "bad dtype %d", dtype);
+  if (n < 0 || (n * elt_bytes(dtype)) % 16) return fail(LORA_E_ARG, "n * element bytes must be a multiple of 16");
+  if (n == 0) return LORA_OK;
+  if (!src || !dst) return fail(LORA_E_ARG, "null device pointer");
+  if (!aligned16(src) || !aligned16(dst)) return fail(LORA_E_ARG, "buffers not 16-byte aligned");
+  return hip_status(launch_debug_decode(dtype, src, n, dst, (hipStream_t)stream), "debug_decode");
 }
 
 }  // extern "C"

@@ -13,7 +13,7 @@ namespace lora {
 // ---- split API: shrink -------------------------------------------------------
 // Block = (token i, group of `rpg` rank rows); groups of one token share an XCD
 // so that x_i is read from HBM once.  Writes v[i][k] for the group's k < v_ld.
-template <typename T, int NT, int U>
+template <typename T, typename X, int NT, int U>
 __global__ __launch_bounds__(NT) void k_bgmv_shrink(PoolView pv, IoDesc io,
                                                     const int32_t* __restrict__ ids, int n,
                                                     float* __restrict__ v, int v_ld, int ngroups,
@@ -31,8 +31,9 @@ __global__ __launch_bounds__(NT) void k_bgmv_shrink(PoolView pv, IoDesc io,
   const int k_end = min(k_lo + rpg, v_ld);
   const int k_hi = max(k_lo, min(e.rank, k_end));
   if (k_lo < k_hi) {
-    const char* xr[1] = {reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * sizeof(T)};
-    valu_shrink<T, NT, U, 1, 16>(pv, e, io.d_in, io.npa, xr, k_lo, k_hi, k_hi, part, vsh, kMaxR);
+    const char* xr[1] = {reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * sizeof(X)};
+    valu_shrink<T, X, NT, U, 1, 16>(pv, e, io.d_in, io.npa, xr, k_lo, k_hi, k_hi, part, vsh, kMaxR,
+                                    kQRow);
   }
   for (int k = k_lo + (int)threadIdx.x; k < k_end; k += NT)
     v[(int64_t)i * v_ld + k] = k < k_hi ? vsh[k] : 0.f;
@@ -57,7 +58,11 @@ __global__ __launch_bounds__(NT) void k_bgmv_expand(PoolView pv, IoDesc io,
   const int m_lo = q * rps;
   const int m_hi = min(io.d_out, m_lo + rps);
   if (m_lo >= m_hi) return;
-  for (int k = threadIdx.x; k < e.rs; k += NT) vsh[k] = k < e.rank ? v[(int64_t)i * v_ld + k] : 0.f;
+  for (int k = threadIdx.x; k < e.rs; k += NT) {
+    float vk = k < e.rank ? v[(int64_t)i * v_ld + k] : 0.f;
+    if constexpr (is_quant<T>()) vk = k < e.rank ? vk * q_scale(pv, e.q_off + e.rank + k) : 0.f;
+    vsh[k] = vk;
+  }
   __syncthreads();
   const float s = tok_scale ? tok_scale[i] : e.scale;
   char* yr[1] = {reinterpret_cast<char*>(io.y) + (int64_t)i * io.d_out * sizeof(TY)};
@@ -71,25 +76,27 @@ __global__ __launch_bounds__(NT) void k_bgmv_expand(PoolView pv, IoDesc io,
 // in flight together.  The splits of a unit share an XCD, so the repeated
 // shrink reads hit that XCD's L2.  MAXN: largest B-row chunk count given a
 // prefetching body in this variant (bigger rows take the plain path).
-template <typename T, typename TY, int NT, int U, int NCH>
+template <typename T, typename X, typename TY, int NT, int U, int NCH>
 __device__ __forceinline__ void bgmv_fused_body(const PoolView& pv, const DevEntry& e,
                                                 const IoDesc& io, int i, int m_lo, int m_hi,
                                                 float* part, float* vsh) {
   constexpr int kKB = U == 1 ? 16 : 8;  // A rows per batch (16-byte loads per thread: kKB * U)
-  const char* xr[1] = {reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * sizeof(T)};
+  const char* xr[1] = {reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * sizeof(X)};
   char* yrow = reinterpret_cast<char*>(io.y) + (int64_t)i * io.d_out * sizeof(TY);
   const float s = e.scale;
   if constexpr (NCH > 0) {
     ExpandPrefetch<T, TY, NT, NCH> pf;
     const int m0 = m_lo + (int)threadIdx.x;
     pf.load(pv, e, yrow, m0, m_hi);
-    valu_shrink<T, NT, U, 1, kKB>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
+    valu_shrink<T, X, NT, U, 1, kKB>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR,
+                                     kQRowCol);
     pf.finish(vsh, s, yrow, m0, m_hi);
     char* yr[1] = {yrow};
     valu_expand<T, TY, NT, NCH, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo + NT * ExpandPrefetch<T, TY, NT, NCH>::RU,
                                    m_hi);
   } else {
-    valu_shrink<T, NT, U, 1, kKB>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
+    valu_shrink<T, X, NT, U, 1, kKB>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR,
+                                     kQRowCol);
     char* yr[1] = {yrow};
     valu_expand<T, TY, NT, 0, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo, m_hi);
   }
@@ -100,12 +107,13 @@ __device__ __forceinline__ void bgmv_fused_body(const PoolView& pv, const DevEnt
 // loads), then x, the first 16 A rows and the first pass of B rows and y are
 // all issued together, so a block waits for one dependent lookup and one data
 // round trip before its first arithmetic.
-template <typename T, typename TY, int NT, int U, int NCH>
+template <typename T, typename X, typename TY, int NT, int U, int NCH>
 __device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEntry& e,
                                                 const IoDesc& io, int i, int m_lo, int m_hi,
                                                 float* part, float* vsh) {
   constexpr int E = ET<T>::E;
   constexpr int ELT = ET<T>::bytes;
+  constexpr int XC = x_chunks<T, X>();
   constexpr int NW = NT / 64;
   constexpr int KB = 16;
   constexpr int RU = rows_per_pass(NCH);
@@ -115,7 +123,7 @@ __device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEnt
   const int C = io.d_in / E;
   const int r = e.rank;
   const int mlast = m_hi - 1;
-  const char* xrow = reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * ELT;
+  const char* xrow = reinterpret_cast<const char*>(io.x) + (int64_t)i * io.d_in * (int)sizeof(X);
   char* yrow = reinterpret_cast<char*>(io.y) + (int64_t)i * io.d_out * sizeof(TY);
   // (1) page ids: B rows (vector loads), the first 16 A rows (scalar loads);
   //     indices are clamped, so every load below is unconditional
@@ -133,9 +141,11 @@ __device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEnt
     cc[u] = cv[u] ? t + NT * u : C - 1;
   }
   // (2) all data of the first pass
-  uint4 xr[U];
+  uint4 xr[U][XC];
 #pragma unroll
-  for (int u = 0; u < U; ++u) xr[u] = ld16(xrow + (int64_t)cc[u] * 16);
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int q = 0; q < XC; ++q) xr[u][q] = ld16(xrow + ((int64_t)cc[u] * XC + q) * 16);
   uint4 a[KB][U];
 #pragma unroll
   for (int kk = 0; kk < KB; ++kk)
@@ -151,12 +161,14 @@ __device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEnt
   }
   // (3) shrink: first 16 rank rows, then the rest of the rank
 #pragma unroll
-  for (int u = 0; u < U; ++u) xr[u] = keep16(xr[u], cv[u]);
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int q = 0; q < XC; ++q) xr[u][q] = keep16(xr[u][q], cv[u]);
 #pragma unroll
   for (int kk = 0; kk < KB; ++kk) {
     float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc = dot16<T>(a[kk][u], xr[u], acc);
+    for (int u = 0; u < U; ++u) acc = dotwx<T, X>(a[kk][u], xr[u], acc);
     const float sum = wave_sum(acc);
     if (lane == 0 && kk < r) part[w * kMaxR + kk] = sum;
   }
@@ -171,7 +183,7 @@ __device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEnt
     for (int kk = 0; kk < KB; ++kk) {
       float acc = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) acc = dot16<T>(a[kk][u], xr[u], acc);
+      for (int u = 0; u < U; ++u) acc = dotwx<T, X>(a[kk][u], xr[u], acc);
       const float sum = wave_sum(acc);
       if (lane == 0 && k0 + kk < r) part[w * kMaxR + k0 + kk] = sum;
     }
@@ -182,6 +194,9 @@ __device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEnt
     if (k < r) {
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) sum += part[ww * kMaxR + k];
+      // quantised pages: v[k] * b_scale[k], ready for the codes of B
+      if constexpr (is_quant<T>())
+        sum *= q_scale(pv, e.q_off + k) * q_scale(pv, e.q_off + r + k);
     }
     vsh[k] = sum;
   }
@@ -200,7 +215,7 @@ __device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEnt
   valu_expand<T, TY, NT, NCH, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo + NT * RU, m_hi);
 }
 
-template <typename T, typename TY, int NT, int U, int MAXN>
+template <typename T, typename X, typename TY, int NT, int U, int MAXN>
 __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
                                                    const int32_t* __restrict__ ids, int n,
                                                    int nsplit, int rps) {
@@ -226,9 +241,9 @@ __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
 #define LORA_FUSED_CASE(N)                                                                   \
   if (N <= MAXN && nch == N) {                                                               \
     if (fast)                                                                                \
-      bgmv_fused_fast<T, TY, NT, U, (N <= MAXN ? N : 1)>(pv, e, io, i, m_lo, m_hi, part, vsh); \
+      bgmv_fused_fast<T, X, TY, NT, U, (N <= MAXN ? N : 1)>(pv, e, io, i, m_lo, m_hi, part, vsh); \
     else                                                                                     \
-      bgmv_fused_body<T, TY, NT, U, (N <= MAXN ? N : 0)>(pv, e, io, i, m_lo, m_hi, part, vsh); \
+      bgmv_fused_body<T, X, TY, NT, U, (N <= MAXN ? N : 0)>(pv, e, io, i, m_lo, m_hi, part, vsh); \
     return;                                                                                  \
   }
   LORA_FUSED_CASE(1)
@@ -237,7 +252,7 @@ __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
   LORA_FUSED_CASE(8)
   LORA_FUSED_CASE(16)
 #undef LORA_FUSED_CASE
-  bgmv_fused_body<T, TY, NT, U, 0>(pv, e, io, i, m_lo, m_hi, part, vsh);
+  bgmv_fused_body<T, X, TY, NT, U, 0>(pv, e, io, i, m_lo, m_hi, part, vsh);
 }
 
 // ---- launchers ----------------------------------------------------------------
@@ -251,7 +266,7 @@ inline int pick_u(int d_in, int E, int NT) {
   return C > NT ? 2 : 1;
 }
 
-template <typename T>
+template <typename T, typename X>
 hipError_t shrink_t(const PoolView& pv, const IoDesc& io, const int32_t* ids, int n, float* v,
                     int v_ld, hipStream_t s) {
   constexpr int E = ET<T>::E;
@@ -263,13 +278,13 @@ hipError_t shrink_t(const PoolView& pv, const IoDesc& io, const int32_t* ids, in
   const dim3 grid(xcd_grid(n, ngroups));
   if (C >= 512) {
     if (pick_u(io.d_in, E, 512) == 1)
-      hipLaunchKernelGGL((k_bgmv_shrink<T, 512, 1>), grid, dim3(512), 0, s, pv, io, ids, n, v,
+      hipLaunchKernelGGL((k_bgmv_shrink<T, X, 512, 1>), grid, dim3(512), 0, s, pv, io, ids, n, v,
                          v_ld, ngroups, rpg);
     else
-      hipLaunchKernelGGL((k_bgmv_shrink<T, 512, 2>), grid, dim3(512), 0, s, pv, io, ids, n, v,
+      hipLaunchKernelGGL((k_bgmv_shrink<T, X, 512, 2>), grid, dim3(512), 0, s, pv, io, ids, n, v,
                          v_ld, ngroups, rpg);
   } else {
-    hipLaunchKernelGGL((k_bgmv_shrink<T, 256, 1>), grid, dim3(256), 0, s, pv, io, ids, n, v,
+    hipLaunchKernelGGL((k_bgmv_shrink<T, X, 256, 1>), grid, dim3(256), 0, s, pv, io, ids, n, v,
                        v_ld, ngroups, rpg);
   }
   return hipGetLastError();
@@ -292,19 +307,22 @@ hipError_t expand_t(const PoolView& pv, const IoDesc& io, const float* v, int v_
   return hipGetLastError();
 }
 
-template <typename T, typename TY, int NT, int U>
+template <typename T, typename X, typename TY, int NT, int U>
 void apply_launch(const PoolView& pv, const IoSet& ios, const int32_t* ids, int n, dim3 grid,
                   int nsplit, int rps, hipStream_t s) {
   // variant by the pool's longest B row, so short-row pools get lean kernels
+  // (FP8 rows of 8 chunks at 512 threads take the loop body: an FP8 chunk
+  // unpacks to twice the values of a 16-bit one)
+  constexpr int kMaxN = (is_quant<T>() && NT == 512) ? 4 : 8;
   if (pv.max_nch <= 2)
-    hipLaunchKernelGGL((k_bgmv_apply<T, TY, NT, U, 2>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
-  else if (pv.max_nch <= 4)
-    hipLaunchKernelGGL((k_bgmv_apply<T, TY, NT, U, 4>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+    hipLaunchKernelGGL((k_bgmv_apply<T, X, TY, NT, U, 2>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+  else if (pv.max_nch <= 4 || kMaxN == 4)
+    hipLaunchKernelGGL((k_bgmv_apply<T, X, TY, NT, U, 4>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
   else
-    hipLaunchKernelGGL((k_bgmv_apply<T, TY, NT, U, 8>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+    hipLaunchKernelGGL((k_bgmv_apply<T, X, TY, NT, U, kMaxN>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
 }
 
-template <typename T, typename TY>
+template <typename T, typename X, typename TY>
 hipError_t apply_t(const PoolView& pv, const IoSet& ios_in, const int32_t* ids, int n,
                    hipStream_t s) {
   constexpr int E = ET<T>::E;
@@ -324,53 +342,68 @@ hipError_t apply_t(const PoolView& pv, const IoSet& ios_in, const int32_t* ids, 
   const dim3 grid(xcd_grid(units, nsplit));
   const int C = ios.max_d_in / E;
   if (C >= 512) {
-    if (pick_u(ios.max_d_in, E, 512) == 1)
-      apply_launch<T, TY, 512, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
+    // FP8: one column chunk per thread (a wider row loops over the columns)
+    if (is_quant<T>() || pick_u(ios.max_d_in, E, 512) == 1)
+      apply_launch<T, X, TY, 512, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
     else
-      apply_launch<T, TY, 512, 2>(pv, ios, ids, n, grid, nsplit, rps, s);
+      apply_launch<T, X, TY, 512, is_quant<T>() ? 1 : 2>(pv, ios, ids, n, grid, nsplit, rps, s);
   } else {
-    apply_launch<T, TY, 256, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
+    apply_launch<T, X, TY, 256, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bgmv_shrink(int dtype, const PoolView& pv, const IoDesc& io,
+hipError_t launch_bgmv_shrink(const Types& ty, const PoolView& pv, const IoDesc& io,
                               const int32_t* ids, int32_t n, float* v, int32_t v_ld,
                               hipStream_t s) {
-  switch (dtype) {
-    case LORA_F32: return shrink_t<float>(pv, io, ids, n, v, v_ld, s);
-    case LORA_F16: return shrink_t<f16_t>(pv, io, ids, n, v, v_ld, s);
-    default: return shrink_t<bf16_t>(pv, io, ids, n, v, v_ld, s);
+  switch (ty.w) {
+    case LORA_F32: return shrink_t<float, float>(pv, io, ids, n, v, v_ld, s);
+    case LORA_F16: return shrink_t<f16_t, f16_t>(pv, io, ids, n, v, v_ld, s);
+    case LORA_BF16: return shrink_t<bf16_t, bf16_t>(pv, io, ids, n, v, v_ld, s);
+    default:
+      return ty.x == LORA_F16 ? shrink_t<fp8_t, f16_t>(pv, io, ids, n, v, v_ld, s)
+                              : shrink_t<fp8_t, bf16_t>(pv, io, ids, n, v, v_ld, s);
   }
 }
 
-hipError_t launch_bgmv_expand(int dtype, int y_dtype, const PoolView& pv, const IoDesc& io,
+hipError_t launch_bgmv_expand(const Types& ty, const PoolView& pv, const IoDesc& io,
                               const float* v, int32_t v_ld, const int32_t* ids, int32_t n,
                               const float* tok_scale, hipStream_t s) {
-  const bool yf = (y_dtype == LORA_F32);
-  switch (dtype) {
+  const bool yf = (ty.y == LORA_F32);
+  switch (ty.w) {
     case LORA_F32: return expand_t<float, float>(pv, io, v, v_ld, ids, n, tok_scale, s);
     case LORA_F16:
       return yf ? expand_t<f16_t, float>(pv, io, v, v_ld, ids, n, tok_scale, s)
                 : expand_t<f16_t, f16_t>(pv, io, v, v_ld, ids, n, tok_scale, s);
-    default:
+    case LORA_BF16:
       return yf ? expand_t<bf16_t, float>(pv, io, v, v_ld, ids, n, tok_scale, s)
                 : expand_t<bf16_t, bf16_t>(pv, io, v, v_ld, ids, n, tok_scale, s);
+    default:
+      if (yf) return expand_t<fp8_t, float>(pv, io, v, v_ld, ids, n, tok_scale, s);
+      return ty.y == LORA_F16 ? expand_t<fp8_t, f16_t>(pv, io, v, v_ld, ids, n, tok_scale, s)
+                              : expand_t<fp8_t, bf16_t>(pv, io, v, v_ld, ids, n, tok_scale, s);
   }
 }
 
-hipError_t launch_bgmv_apply(int dtype, int y_dtype, const PoolView& pv, const IoSet& ios,
+hipError_t launch_bgmv_apply(const Types& ty, const PoolView& pv, const IoSet& ios,
                              const int32_t* ids, int32_t n, hipStream_t s) {
-  const bool yf = (y_dtype == LORA_F32);
-  switch (dtype) {
-    case LORA_F32: return apply_t<float, float>(pv, ios, ids, n, s);
+  const bool yf = (ty.y == LORA_F32);
+  switch (ty.w) {
+    case LORA_F32: return apply_t<float, float, float>(pv, ios, ids, n, s);
     case LORA_F16:
-      return yf ? apply_t<f16_t, float>(pv, ios, ids, n, s) : apply_t<f16_t, f16_t>(pv, ios, ids, n, s);
+      return yf ? apply_t<f16_t, f16_t, float>(pv, ios, ids, n, s)
+                : apply_t<f16_t, f16_t, f16_t>(pv, ios, ids, n, s);
+    case LORA_BF16:
+      return yf ? apply_t<bf16_t, bf16_t, float>(pv, ios, ids, n, s)
+                : apply_t<bf16_t, bf16_t, bf16_t>(pv, ios, ids, n, s);
     default:
-      return yf ? apply_t<bf16_t, float>(pv, ios, ids, n, s)
-                : apply_t<bf16_t, bf16_t>(pv, ios, ids, n, s);
+      if (ty.x == LORA_F16)
+        return yf ? apply_t<fp8_t, f16_t, float>(pv, ios, ids, n, s)
+                  : apply_t<fp8_t, f16_t, f16_t>(pv, ios, ids, n, s);
+      return yf ? apply_t<fp8_t, bf16_t, float>(pv, ios, ids, n, s)
+                : apply_t<fp8_t, bf16_t, bf16_t>(pv, ios, ids, n, s);
   }
 }
 

@@ -27,7 +27,7 @@ __device__ __forceinline__ int split_rows(int d_out, int nsplit) {
 // ---- shrink -------------------------------------------------------------------
 // Short items: block = (item, group of rank rows).  MFMA tiles: block = (tile,
 // 32-token half).  v rows are indexed by original token.
-template <typename T, int U>
+template <typename T, typename X, int U>
 __global__ __launch_bounds__(kSgNT) void k_sgmv_shrink_short(PoolView pv, PlanView pl, IoDesc io,
                                                              float* __restrict__ v, int v_ld,
                                                              int first, int count, int ngroups,
@@ -52,10 +52,10 @@ __global__ __launch_bounds__(kSgNT) void k_sgmv_shrink_short(PoolView pv, PlanVi
     const char* xr[kShortG];
 #pragma unroll
     for (int g = 0; g < kShortG; ++g)
-      xr[g] = tok[g] >= 0 ? reinterpret_cast<const char*>(io.x) + (int64_t)tok[g] * io.d_in * sizeof(T)
+      xr[g] = tok[g] >= 0 ? reinterpret_cast<const char*>(io.x) + (int64_t)tok[g] * io.d_in * sizeof(X)
                           : nullptr;
-    valu_shrink<T, kSgNT, U, kShortG, 8>(pv, e, io.d_in, io.npa, xr, k_lo, k_hi, k_hi, part, vsh,
-                                         kMaxR);
+    valu_shrink<T, X, kSgNT, U, kShortG, 8>(pv, e, io.d_in, io.npa, xr, k_lo, k_hi, k_hi, part, vsh,
+                                            kMaxR, kQRow);
   }
   const int nk = k_end - k_lo;
   for (int idx = threadIdx.x; idx < kShortG * nk; idx += kSgNT) {
@@ -88,7 +88,10 @@ __global__ __launch_bounds__(kSgNT, 2) void k_sgmv_expand_short(PoolView pv, Pla
   for (int idx = threadIdx.x; idx < kShortG * e.rs; idx += kSgNT) {
     const int g = idx / e.rs;
     const int k = idx - g * e.rs;
-    vsh[g * kMaxR + k] = (tok[g] >= 0 && k < e.rank) ? v[(int64_t)tok[g] * v_ld + k] : 0.f;
+    float vk = (tok[g] >= 0 && k < e.rank) ? v[(int64_t)tok[g] * v_ld + k] : 0.f;
+    // quantised pages: v[k] * b_scale[k], ready for the codes of B
+    if constexpr (is_quant<T>()) vk = k < e.rank ? vk * q_scale(pv, e.q_off + e.rank + k) : 0.f;
+    vsh[g * kMaxR + k] = vk;
   }
   __syncthreads();
   char* yr[kShortG];
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(kSgNT, 2) void k_sgmv_expand_short(PoolView pv, Pla
 // ---- fused apply ----------------------------------------------------------------
 // Block = ((item, slice) unit, output-row split).  The shrink result never leaves
 // the block (LDS).
-template <typename T, typename TY, int U>
+template <typename T, typename X, typename TY, int U>
 __global__ __launch_bounds__(kSgNT, 2) void k_apply_short(PoolView pv, PlanView pl, IoSet ios,
                                                           int first, int count, int nsplit) {
   __shared__ __attribute__((aligned(16))) char lds[kShortLds];
@@ -131,11 +134,12 @@ __global__ __launch_bounds__(kSgNT, 2) void k_apply_short(PoolView pv, PlanView 
   float sg[kShortG];
 #pragma unroll
   for (int g = 0; g < kShortG; ++g) {
-    xr[g] = tok[g] >= 0 ? reinterpret_cast<const char*>(io.x) + (int64_t)tok[g] * io.d_in * sizeof(T) : nullptr;
+    xr[g] = tok[g] >= 0 ? reinterpret_cast<const char*>(io.x) + (int64_t)tok[g] * io.d_in * sizeof(X) : nullptr;
     yr[g] = tok[g] >= 0 ? reinterpret_cast<char*>(io.y) + (int64_t)tok[g] * io.d_out * sizeof(TY) : nullptr;
     sg[g] = e.scale;
   }
-  valu_shrink<T, kSgNT, U, kShortG, 8>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh, kMaxR);
+  valu_shrink<T, X, kSgNT, U, kShortG, 8>(pv, e, io.d_in, io.npa, xr, 0, e.rank, e.rs, part, vsh,
+                                          kMaxR, kQRowCol);
   valu_expand_any<T, TY, kSgNT, kShortG>(pv, e, vsh, kMaxR, sg, yr, m_lo, m_hi);
 }
 
@@ -214,7 +218,7 @@ inline int pick_nsplit(int units, int d_out, int target, int min_rows) {
   return nsplit;
 }
 
-template <typename T>
+template <typename T, typename X>
 hipError_t shrink_t(const PoolView& pv, const PlanView& pl, const IoDesc& io, float* v, int v_ld,
                     hipStream_t s) {
   constexpr int E = ET<T>::E;
@@ -231,10 +235,10 @@ hipError_t shrink_t(const PoolView& pv, const PlanView& pl, const IoDesc& io, fl
     const int ngroups = (v_ld + rpg - 1) / rpg;
     const dim3 grid(xcd_grid(n_short, ngroups));
     if (sg_u(io.d_in, E) == 1)
-      hipLaunchKernelGGL((k_sgmv_shrink_short<T, 1>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld,
+      hipLaunchKernelGGL((k_sgmv_shrink_short<T, X, 1>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld,
                          pl.n_mfma, n_short, ngroups, rpg);
     else
-      hipLaunchKernelGGL((k_sgmv_shrink_short<T, 2>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld,
+      hipLaunchKernelGGL((k_sgmv_shrink_short<T, X, 2>), grid, dim3(kSgNT), 0, s, pv, pl, io, v, v_ld,
                          pl.n_mfma, n_short, ngroups, rpg);
   }
   return hipGetLastError();
@@ -257,7 +261,7 @@ hipError_t expand_t(const PoolView& pv, const PlanView& pl, const IoDesc& io, co
   return hipGetLastError();
 }
 
-template <typename T, typename TY>
+template <typename T, typename X, typename TY>
 hipError_t apply_t(const PoolView& pv, const PlanView& pl, const IoSet& ios, hipStream_t s) {
   constexpr int E = ET<T>::E;
   const int n_short = pl.n_items - pl.n_mfma;
@@ -272,10 +276,10 @@ hipError_t apply_t(const PoolView& pv, const PlanView& pl, const IoSet& ios, hip
     const int nsplit = pick_nsplit(units, ios.max_d_out, 512, 2048);
     const dim3 grid(xcd_grid(units, nsplit));
     if (sg_u(ios.max_d_in, E) == 1)
-      hipLaunchKernelGGL((k_apply_short<T, TY, 1>), grid, dim3(kSgNT), 0, s, pv, pl, ios, pl.n_mfma,
+      hipLaunchKernelGGL((k_apply_short<T, X, TY, 1>), grid, dim3(kSgNT), 0, s, pv, pl, ios, pl.n_mfma,
                          n_short, nsplit);
     else
-      hipLaunchKernelGGL((k_apply_short<T, TY, 2>), grid, dim3(kSgNT), 0, s, pv, pl, ios, pl.n_mfma,
+      hipLaunchKernelGGL((k_apply_short<T, X, TY, 2>), grid, dim3(kSgNT), 0, s, pv, pl, ios, pl.n_mfma,
                          n_short, nsplit);
   }
   return hipGetLastError();
@@ -283,40 +287,54 @@ hipError_t apply_t(const PoolView& pv, const PlanView& pl, const IoSet& ios, hip
 
 }  // namespace
 
-hipError_t launch_sgmv_shrink(int dtype, const PoolView& pv, const PlanView& pl, const IoDesc& io,
-                              float* v, int32_t v_ld, hipStream_t s) {
+hipError_t launch_sgmv_shrink(const Types& ty, const PoolView& pv, const PlanView& pl,
+                              const IoDesc& io, float* v, int32_t v_ld, hipStream_t s) {
   if (pl.n_items == 0) return hipSuccess;
-  switch (dtype) {
-    case LORA_F32: return shrink_t<float>(pv, pl, io, v, v_ld, s);
-    case LORA_F16: return shrink_t<f16_t>(pv, pl, io, v, v_ld, s);
-    default: return shrink_t<bf16_t>(pv, pl, io, v, v_ld, s);
+  switch (ty.w) {
+    case LORA_F32: return shrink_t<float, float>(pv, pl, io, v, v_ld, s);
+    case LORA_F16: return shrink_t<f16_t, f16_t>(pv, pl, io, v, v_ld, s);
+    case LORA_BF16: return shrink_t<bf16_t, bf16_t>(pv, pl, io, v, v_ld, s);
+    default:
+      return ty.x == LORA_F16 ? shrink_t<fp8_t, f16_t>(pv, pl, io, v, v_ld, s)
+                              : shrink_t<fp8_t, bf16_t>(pv, pl, io, v, v_ld, s);
   }
 }
 
-hipError_t launch_sgmv_expand(int dtype, int y_dtype, const PoolView& pv, const PlanView& pl,
+hipError_t launch_sgmv_expand(const Types& ty, const PoolView& pv, const PlanView& pl,
                               const IoDesc& io, const float* v, int32_t v_ld, hipStream_t s) {
   if (pl.n_items == 0) return hipSuccess;
-  const bool yf = (y_dtype == LORA_F32);
-  switch (dtype) {
+  const bool yf = (ty.y == LORA_F32);
+  switch (ty.w) {
     case LORA_F32: return expand_t<float, float>(pv, pl, io, v, v_ld, s);
     case LORA_F16:
       return yf ? expand_t<f16_t, float>(pv, pl, io, v, v_ld, s) : expand_t<f16_t, f16_t>(pv, pl, io, v, v_ld, s);
-    default:
+    case LORA_BF16:
       return yf ? expand_t<bf16_t, float>(pv, pl, io, v, v_ld, s)
                 : expand_t<bf16_t, bf16_t>(pv, pl, io, v, v_ld, s);
+    default:
+      if (yf) return expand_t<fp8_t, float>(pv, pl, io, v, v_ld, s);
+      return ty.y == LORA_F16 ? expand_t<fp8_t, f16_t>(pv, pl, io, v, v_ld, s)
+                              : expand_t<fp8_t, bf16_t>(pv, pl, io, v, v_ld, s);
   }
 }
 
-hipError_t launch_apply(int dtype, int y_dtype, const PoolView& pv, const PlanView& pl,
-                        const IoSet& ios, hipStream_t s) {
+hipError_t launch_apply(const Types& ty, const PoolView& pv, const PlanView& pl, const IoSet& ios,
+                        hipStream_t s) {
   if (pl.n_items == 0) return hipSuccess;
-  const bool yf = (y_dtype == LORA_F32);
-  switch (dtype) {
-    case LORA_F32: return apply_t<float, float>(pv, pl, ios, s);
+  const bool yf = (ty.y == LORA_F32);
+  switch (ty.w) {
+    case LORA_F32: return apply_t<float, float, float>(pv, pl, ios, s);
     case LORA_F16:
-      return yf ? apply_t<f16_t, float>(pv, pl, ios, s) : apply_t<f16_t, f16_t>(pv, pl, ios, s);
+      return yf ? apply_t<f16_t, f16_t, float>(pv, pl, ios, s) : apply_t<f16_t, f16_t, f16_t>(pv, pl, ios, s);
+    case LORA_BF16:
+      return yf ? apply_t<bf16_t, bf16_t, float>(pv, pl, ios, s)
+                : apply_t<bf16_t, bf16_t, bf16_t>(pv, pl, ios, s);
     default:
-      return yf ? apply_t<bf16_t, float>(pv, pl, ios, s) : apply_t<bf16_t, bf16_t>(pv, pl, ios, s);
+      if (ty.x == LORA_F16)
+        return yf ? apply_t<fp8_t, f16_t, float>(pv, pl, ios, s)
+                  : apply_t<fp8_t, f16_t, f16_t>(pv, pl, ios, s);
+      return yf ? apply_t<fp8_t, bf16_t, float>(pv, pl, ios, s)
+                : apply_t<fp8_t, bf16_t, bf16_t>(pv, pl, ios, s);
   }
 }
 

@@ -27,6 +27,7 @@ __global__ void k_scatter_pages(char* __restrict__ pages, int64_t page_bytes,
 }
 
 static uint32_t pattern_word(uint32_t pattern, int elt) {
+  if (elt == 1) return (pattern & 0xffu) * 0x01010101u;
   return elt == 4 ? pattern : (pattern & 0xffffu) | (pattern << 16);
 }
 
@@ -98,9 +99,38 @@ __global__ void k_debug_gather(PoolView pv, IoDesc io, int elt, int adapter, int
     }
     if (elt == 4)
       *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
-    else
+    else if (elt == 2)
       *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
+    else
+      *dst = *src;
   }
+}
+
+// Stored elements -> fp32 through the compute kernels' own decoder (unpack16),
+// one 16-byte chunk per thread.
+template <typename T>
+__global__ void k_debug_decode(const char* __restrict__ src, int64_t nchunks, float* __restrict__ dst) {
+  const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (c >= nchunks) return;
+  float f[ET<T>::E];
+  unpack16<T>(ld16(src + c * 16), f);
+#pragma unroll
+  for (int e = 0; e < ET<T>::E; ++e) dst[c * ET<T>::E + e] = f[e];
+}
+
+hipError_t launch_debug_decode(int dtype, const void* src, int64_t n, float* dst, hipStream_t s) {
+  const int elt = dtype == LORA_F32 ? 4 : (dtype == LORA_FP8_E4M3 ? 1 : 2);
+  const int64_t nchunks = n * elt / 16;
+  if (nchunks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((nchunks + 255) / 256));
+  const char* p = reinterpret_cast<const char*>(src);
+  switch (dtype) {
+    case LORA_F32: hipLaunchKernelGGL(k_debug_decode<float>, grid, dim3(256), 0, s, p, nchunks, dst); break;
+    case LORA_F16: hipLaunchKernelGGL(k_debug_decode<f16_t>, grid, dim3(256), 0, s, p, nchunks, dst); break;
+    case LORA_BF16: hipLaunchKernelGGL(k_debug_decode<bf16_t>, grid, dim3(256), 0, s, p, nchunks, dst); break;
+    default: hipLaunchKernelGGL(k_debug_decode<fp8_t>, grid, dim3(256), 0, s, p, nchunks, dst); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_debug_resolve(const PoolView& pv, const IoDesc& io, int32_t max_rank, int elt,

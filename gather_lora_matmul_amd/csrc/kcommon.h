@@ -19,6 +19,10 @@ struct f16_t {
 struct bf16_t {
   uint16_t b;
 };
+// OCP FP8 E4M3 adapter codes (quantised pools; per-row scales in the table)
+struct fp8_t {
+  uint8_t b;
+};
 
 template <typename T>
 struct ET;
@@ -37,6 +41,21 @@ struct ET<bf16_t> {
   static constexpr int E = 8;
   static constexpr int bytes = 2;
 };
+template <>
+struct ET<fp8_t> {
+  static constexpr int E = 16;
+  static constexpr int bytes = 1;
+};
+template <typename T>
+constexpr bool is_quant() {
+  return ET<T>::bytes == 1;
+}
+// 16-byte chunks of x (activation type X) that cover the columns of one
+// 16-byte chunk of a weight row (type T): 2 for FP8 codes with 16-bit x.
+template <typename T, typename X>
+constexpr int x_chunks() {
+  return ET<X>::bytes / ET<T>::bytes;
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -73,6 +92,38 @@ __device__ __forceinline__ void unpack16<f16_t>(const uint4 u, float* f) {
     f[2 * i] = (float)h.x;
     f[2 * i + 1] = (float)h.y;
   }
+}
+
+// 16 FP8 E4M3 codes -> floats with the hardware conversion (two codes per
+// instruction; NaN codes stay NaN, subnormals are exact).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <>
+__device__ __forceinline__ void unpack16<fp8_t>(const uint4 u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    f[4 * i] = lo.x;
+    f[4 * i + 1] = lo.y;
+    f[4 * i + 2] = hi.x;
+    f[4 * i + 3] = hi.y;
+  }
+}
+
+// acc + sum_e a[e] * x[e] over the E_T columns of one 16-byte weight chunk, x
+// given as x_chunks<T, X>() 16-byte chunks of activations, ascending e.
+template <typename T, typename X>
+__device__ __forceinline__ float dotwx(const uint4 a, const uint4* x, float acc) {
+  constexpr int E = ET<T>::E;
+  constexpr int XC = x_chunks<T, X>();
+  float fa[E], fx[E];
+  unpack16<T>(a, fa);
+#pragma unroll
+  for (int q = 0; q < XC; ++q) unpack16<X>(x[q], fx + q * ET<X>::E);
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc = __builtin_fmaf(fa[e], fx[e], acc);
+  return acc;
 }
 
 // acc + sum_e a[e] * b[e] over one 16-byte chunk pair, ascending e.
@@ -186,6 +237,12 @@ __device__ __forceinline__ bool adapter_in_table(const PoolView& pv, int a) {
 __device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int idx) {
   typedef const __attribute__((address_space(4))) int32_t* cptr;
   return ((cptr)p)[idx];
+}
+
+// Quantised adapters: the per-rank scales follow the page ids in the same
+// table, as float bits: a_scale[k] at q_off + k, b_scale[k] at q_off + rank + k.
+__device__ __forceinline__ float q_scale(const PoolView& pv, int idx) {
+  return __int_as_float(pv.page_ids[idx]);
 }
 
 // Byte offset (from the pool base) of element j of A row k.

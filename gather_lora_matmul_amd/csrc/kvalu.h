@@ -25,17 +25,24 @@ __device__ __forceinline__ uint4 keep16(uint4 v, bool keep) {
   return keep ? v : make_uint4(0, 0, 0, 0);
 }
 
+// Scale modes of a quantised shrink (ignored for 16/32-bit pages): the sum
+// over the codes of A row k is multiplied by a_scale[k] (the true v[k]), or by
+// a_scale[k] * b_scale[k] when the expand that follows reads codes of B.
+constexpr int kQNone = 0, kQRow = 1, kQRowCol = 2;
+
 // vsh[g*VS + k] = sum_j A[k][j] * x_g[j] for k in [k_lo, k_hi); zero for k in
-// [k_hi, k_zero).  xrow[g] == nullptr marks an unused token slot (xrow[0] must
-// be valid).  part: LDS scratch of (NT/64) * G * kMaxR floats.  Must be called
-// by the whole block with block-uniform arguments (it contains barriers).
-template <typename T, int NT, int U, int G, int KB>
+// [k_hi, k_zero).  T: page type, X: activation type of x.  xrow[g] == nullptr
+// marks an unused token slot (xrow[0] must be valid).  part: LDS scratch of
+// (NT/64) * G * kMaxR floats.  Must be called by the whole block with
+// block-uniform arguments (it contains barriers).
+template <typename T, typename X, int NT, int U, int G, int KB>
 __device__ __forceinline__ void valu_shrink(const PoolView& pv, const DevEntry& e, int d_in,
                                             int npa, const char* const* xrow, int k_lo,
                                             int k_hi, int k_zero, float* part, float* vsh,
-                                            int VS) {
+                                            int VS, int qmode = kQNone) {
   constexpr int E = ET<T>::E;
   constexpr int ELT = ET<T>::bytes;
+  constexpr int XC = x_chunks<T, X>();
   constexpr int NW = NT / 64;
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -79,21 +86,25 @@ __device__ __forceinline__ void valu_shrink(const PoolView& pv, const DevEntry& 
           for (int u = 0; u < U; ++u)
             a[kk][u] = ld16(pv.pages + a_offset(pv, e, npa, ELT, min(k0 + kk, k_hi - 1), cc[u] * E));
       }
-      uint4 xr[G][U];
+      uint4 xr[G][U][XC];
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int u = 0; u < U; ++u) xr[g][u] = ld16(xs[g] + (int64_t)cc[u] * 16);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < XC; ++q) xr[g][u][q] = ld16(xs[g] + ((int64_t)cc[u] * XC + q) * 16);
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int u = 0; u < U; ++u) xr[g][u] = keep16(xr[g][u], xv[g] && cv[u]);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < XC; ++q) xr[g][u][q] = keep16(xr[g][u][q], xv[g] && cv[u]);
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int u = 0; u < U; ++u) acc[g][kk] = dot16<T>(a[kk][u], xr[g][u], acc[g][kk]);
+          for (int u = 0; u < U; ++u) acc[g][kk] = dotwx<T, X>(a[kk][u], xr[g][u], acc[g][kk]);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -111,6 +122,13 @@ __device__ __forceinline__ void valu_shrink(const PoolView& pv, const DevEntry& 
     float s = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) s += part[(ww * G + g) * kMaxR + kk];
+    if constexpr (is_quant<T>()) {
+      if (qmode != kQNone) {
+        float f = q_scale(pv, e.q_off + k_lo + kk);
+        if (qmode == kQRowCol) f *= q_scale(pv, e.q_off + e.rank + k_lo + kk);
+        s *= f;
+      }
+    }
     vsh[g * VS + k_lo + kk] = s;
   }
   const int nz = k_zero - k_hi;
@@ -249,7 +267,16 @@ __device__ __forceinline__ void valu_expand_any(const PoolView& pv, const DevEnt
   case N:                \
     valu_expand<T, TY, NT, N, G>(pv, e, vsh, VS, sg, yrow, m_lo, m_hi); \
     break;
-  if constexpr (G > 1) {
+  if constexpr (G > 1 && is_quant<T>()) {
+    // an FP8 chunk unpacks to 16 values: the same rank span as 2 chunks of
+    // 16-bit pages, so half the unrolled chunk counts keep the registers
+    switch (nch) {
+      LORA_NCH_CASE(1)
+      LORA_NCH_CASE(2)
+      default:
+        valu_expand<T, TY, NT, 0, G>(pv, e, vsh, VS, sg, yrow, m_lo, m_hi);
+    }
+  } else if constexpr (G > 1 || is_quant<T>()) {
     switch (nch) {
       LORA_NCH_CASE(1)
       LORA_NCH_CASE(2)

@@ -22,7 +22,8 @@ struct DevEntry {
   int32_t a_off;   // index of the adapter's first A page id in the page-id list
   int32_t b_off;   // index of its first B page id
   float inv_rpp;   // 1.0f / rpp (quotient estimate, corrected exactly)
-  int32_t pad;
+  int32_t q_off;   // quantised pools: index of the adapter's scales in the
+                   // page-id list (rank a_scale words, then rank b_scale words)
 };
 static_assert(sizeof(DevEntry) == 32, "DevEntry must stay 32 bytes");
 
@@ -68,6 +69,12 @@ constexpr int kShortG = 4;   // tokens per short item
 constexpr int kTileM = 64;   // tokens per MFMA tile
 constexpr int kMaxNpa = 8;            // MFMA tiles: pages per A row, at most
 
+// Element types of one call: pages (w), activations x (x) and y (y), as
+// lora_dtype codes.  x equals w except on FP8 pools (16-bit x).
+struct Types {
+  int w, x, y;
+};
+
 // ---- kernel launchers (defined in the .hip files) -------------------------
 hipError_t launch_fill_pages(char* pages, int64_t page_bytes, const int32_t* ids_dev,
                              int64_t n, uint32_t pattern, int elt, hipStream_t s);
@@ -76,13 +83,13 @@ hipError_t launch_fill_all(char* pages, int64_t bytes, uint32_t pattern, int elt
 hipError_t launch_scatter_pages(char* pages, int64_t page_bytes, const char* staging,
                                 const int32_t* ids_dev, int64_t n, hipStream_t s);
 
-hipError_t launch_bgmv_shrink(int dtype, const PoolView& pv, const IoDesc& io,
+hipError_t launch_bgmv_shrink(const Types& ty, const PoolView& pv, const IoDesc& io,
                               const int32_t* ids, int32_t n, float* v, int32_t v_ld,
                               hipStream_t s);
-hipError_t launch_bgmv_expand(int dtype, int y_dtype, const PoolView& pv, const IoDesc& io,
+hipError_t launch_bgmv_expand(const Types& ty, const PoolView& pv, const IoDesc& io,
                               const float* v, int32_t v_ld, const int32_t* ids, int32_t n,
                               const float* tok_scale, hipStream_t s);
-hipError_t launch_bgmv_apply(int dtype, int y_dtype, const PoolView& pv, const IoSet& ios,
+hipError_t launch_bgmv_apply(const Types& ty, const PoolView& pv, const IoSet& ios,
                              const int32_t* ids, int32_t n, hipStream_t s);
 
 // Position in a launch's sequence of MFMA work for the persistent kernels:
@@ -120,12 +127,15 @@ struct PlanView {
   int32_t G;                   // persistent grid (blocks)
 };
 
-hipError_t launch_sgmv_shrink(int dtype, const PoolView& pv, const PlanView& pl,
+hipError_t launch_sgmv_shrink(const Types& ty, const PoolView& pv, const PlanView& pl,
                               const IoDesc& io, float* v, int32_t v_ld, hipStream_t s);
-hipError_t launch_sgmv_expand(int dtype, int y_dtype, const PoolView& pv, const PlanView& pl,
+hipError_t launch_sgmv_expand(const Types& ty, const PoolView& pv, const PlanView& pl,
                               const IoDesc& io, const float* v, int32_t v_ld, hipStream_t s);
-hipError_t launch_apply(int dtype, int y_dtype, const PoolView& pv, const PlanView& pl,
+hipError_t launch_apply(const Types& ty, const PoolView& pv, const PlanView& pl,
                         const IoSet& ios, hipStream_t s);
+// Decode n stored elements of `dtype` to fp32 with the kernels' decoder
+// (n * element bytes a multiple of 16).
+hipError_t launch_debug_decode(int dtype, const void* src, int64_t n, float* dst, hipStream_t s);
 
 hipError_t launch_debug_resolve(const PoolView& pv, const IoDesc& io, int32_t max_rank,
                                 int elt, const int32_t* ids, int32_t n, int64_t* a_off,

@@ -229,7 +229,8 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
       pl->h_perm[(size_t)cur[(size_t)b]++] = i;
     }
   }
-  const bool mfma_ok = (p->dtype != LORA_F32);
+  // MFMA tiles for 16-bit pages; fp32 and FP8 pages run as short VALU items
+  const bool mfma_ok = (p->dtype == LORA_F16 || p->dtype == LORA_BF16);
   struct Keyed {
     PlanItem it;
     int band;

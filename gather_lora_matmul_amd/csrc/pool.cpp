@@ -36,7 +36,9 @@ static uint64_t splitmix64(uint64_t& s) {
 }
 
 static void fill_pattern(char* dst, size_t bytes, uint32_t pattern, int elt) {
-  if (elt == 4) {
+  if (elt == 1) {
+    memset(dst, (int)(pattern & 0xffu), bytes);
+  } else if (elt == 4) {
     for (size_t i = 0; i + 4 <= bytes; i += 4) memcpy(dst + i, &pattern, 4);
   } else {
     const uint16_t p16 = (uint16_t)pattern;
@@ -88,7 +90,10 @@ lora_status lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
   clear_error();
   if (!d || !out) return fail(LORA_E_ARG, "null argument");
   *out = nullptr;
-  if (d->dtype < LORA_F32 || d->dtype > LORA_BF16) return fail(LORA_E_ARG, "bad dtype %d", d->dtype);
+  if (d->dtype < LORA_F32 || d->dtype > LORA_FP8_E4M3) return fail(LORA_E_ARG, "bad dtype %d", d->dtype);
+  const bool quant = d->dtype == LORA_FP8_E4M3;
+  if (quant ? (d->act_dtype != LORA_F16 && d->act_dtype != LORA_BF16) : d->act_dtype != d->dtype)
+    return fail(LORA_E_ARG, "act_dtype %d: the page dtype, or f16/bf16 for FP8 pages", d->act_dtype);
   const int elt = elt_bytes(d->dtype);
   if (d->page_elems <= 0 || ((int64_t)d->page_elems * elt) % 16 != 0)
     return fail(LORA_E_ARG, "page_elems %d: page size must be a positive multiple of 16 bytes",
@@ -103,9 +108,10 @@ lora_status lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
   if (host_only && d->pages_dev) return fail(LORA_E_ARG, "host-only pool takes no device pages");
   for (int s = 0; s < d->n_slices; ++s) {
     if (d->slice_d_in[s] <= 0 || d->slice_d_out[s] <= 0 || d->slice_d_in[s] % 8 ||
-        d->slice_d_out[s] % 8 || d->slice_d_out[s] >= (1 << 20) || d->slice_d_in[s] >= (1 << 24))
-      return fail(LORA_E_ARG, "slice %d dims %dx%d: need positive multiples of 8, d_out < 2^20", s,
-                  d->slice_d_in[s], d->slice_d_out[s]);
+        d->slice_d_out[s] % 8 || d->slice_d_out[s] >= (1 << 20) || d->slice_d_in[s] >= (1 << 24) ||
+        (quant && d->slice_d_in[s] % 16))
+      return fail(LORA_E_ARG, "slice %d dims %dx%d: need positive multiples of 8 (d_in of 16 on "
+                  "FP8 pools), d_out < 2^20", s, d->slice_d_in[s], d->slice_d_out[s]);
   }
   {
     // the largest rank must fit one B row per page
@@ -117,6 +123,7 @@ lora_status lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
   if (!p) return fail(LORA_E_NOMEM, "out of host memory");
   p->P = d->page_elems;
   p->dtype = d->dtype;
+  p->act = d->act_dtype;
   p->n_pages = d->n_pages;
   p->max_adapters = d->max_adapters;
   p->max_rank = d->max_rank;
@@ -185,8 +192,10 @@ lora_status lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
       return st;
     }
   }
+  // page ids of every page, plus (FP8) 2 * max_rank scale words per slot
+  p->page_ids_cap = (size_t)p->n_pages + (quant ? 2 * (size_t)p->max_rank * p->slots.size() : 0);
   e = hipMalloc((void**)&p->d_entries, sizeof(DevEntry) * p->slots.size());
-  if (e == hipSuccess) e = hipMalloc((void**)&p->d_page_ids, sizeof(int32_t) * (size_t)p->n_pages);
+  if (e == hipSuccess) e = hipMalloc((void**)&p->d_page_ids, sizeof(int32_t) * p->page_ids_cap);
   if (e == hipSuccess && poison) e = launch_fill_all(p->pages, bytes, nan_pattern(p->dtype), elt, nullptr);
   if (e == hipSuccess) e = hipMemset(p->d_entries, 0, sizeof(DevEntry) * p->slots.size());
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -257,9 +266,12 @@ lora_status lora_pool_free_pages(lora_pool* p, int64_t n, const int32_t* ids) {
   return LORA_OK;
 }
 
-lora_status lora_pool_upload(lora_pool* p, int32_t adapter, int32_t slice, int32_t rank,
-                             float scale, const void* A, const void* B, void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace lora {
+static lora_status upload_impl(lora_pool* p, int32_t adapter, int32_t slice, int32_t rank,
+                               float scale, const void* A, const float* sa, const void* B,
+                               const float* sb, void* stream) {
   if (!p || !A || !B) return fail(LORA_E_ARG, "null argument");
   if (adapter < 0 || adapter >= p->max_adapters) return fail(LORA_E_ARG, "adapter %d out of range", adapter);
   if (slice < 0 || slice >= p->n_slices) return fail(LORA_E_ARG, "slice %d out of range", slice);
@@ -333,10 +345,38 @@ lora_status lora_pool_upload(lora_pool* p, int32_t adapter, int32_t slice, int32
   sl.rs = rs;
   sl.scale = scale;
   sl.pages = std::move(pages);
+  sl.qs.clear();
+  if (p->quant()) {
+    sl.qs.assign(sa, sa + rank);
+    sl.qs.insert(sl.qs.end(), sb, sb + rank);
+  }
   p->dirty = true;
   ++p->generation;
   return LORA_OK;
 }
+}  // namespace lora
+
+extern "C" {
+
+lora_status lora_pool_upload(lora_pool* p, int32_t adapter, int32_t slice, int32_t rank,
+                             float scale, const void* A, const void* B, void* stream) {
+  clear_error();
+  if (p && p->quant())
+    return fail(LORA_E_ARG, "FP8 pool: upload codes with their scales (lora_pool_upload_scaled)");
+  return upload_impl(p, adapter, slice, rank, scale, A, nullptr, B, nullptr, stream);
+}
+
+lora_status lora_pool_upload_scaled(lora_pool* p, int32_t adapter, int32_t slice, int32_t rank,
+                                    float scale, const void* A, const float* a_scale,
+                                    const void* B, const float* b_scale, void* stream) {
+  clear_error();
+  if (!p) return fail(LORA_E_ARG, "null pool");
+  if (!p->quant()) return fail(LORA_E_ARG, "scaled upload needs an FP8 pool");
+  if (!a_scale || !b_scale) return fail(LORA_E_ARG, "null scale array");
+  return upload_impl(p, adapter, slice, rank, scale, A, a_scale, B, b_scale, stream);
+}
+
+
 
 lora_status lora_pool_evict(lora_pool* p, int32_t adapter, int32_t slice, void* stream) {
   clear_error();
@@ -397,7 +437,17 @@ lora_status lora_page_table_build(lora_pool* p, void* stream) {
       e.a_off = (int32_t)ids.size();
       e.b_off = e.a_off + sl.rank * p->npa[s];
       ids.insert(ids.end(), sl.pages.begin(), sl.pages.end());
+      if (p->quant()) {  // a_scale, then b_scale, as float bits
+        e.q_off = (int32_t)ids.size();
+        for (float f : sl.qs) {
+          int32_t w;
+          memcpy(&w, &f, 4);
+          ids.push_back(w);
+        }
+      }
     }
+  if (!p->host_only && ids.size() > p->page_ids_cap)
+    return fail(LORA_E_STATE, "page table of %zu words exceeds its %zu", ids.size(), p->page_ids_cap);
   if (!p->host_only) {
     const size_t eb = sizeof(DevEntry) * ent.size();
     const size_t ib = sizeof(int32_t) * ids.size();
@@ -431,6 +481,20 @@ lora_status lora_pool_export_entry(const lora_pool* p, int32_t adapter, int32_t 
   if (n_b) *n_b = nb;
   if (a_pages && na) memcpy(a_pages, sl.pages.data(), sizeof(int32_t) * (size_t)na);
   if (b_pages && nb) memcpy(b_pages, sl.pages.data() + na, sizeof(int32_t) * (size_t)nb);
+  return LORA_OK;
+}
+
+lora_status lora_pool_export_scales(const lora_pool* p, int32_t adapter, int32_t slice,
+                                    float* a_scale, float* b_scale) {
+  clear_error();
+  if (!p) return fail(LORA_E_ARG, "null pool");
+  if (!p->quant()) return fail(LORA_E_ARG, "pool is not FP8: no scales");
+  if (adapter < 0 || adapter >= p->max_adapters) return fail(LORA_E_ARG, "adapter %d out of range", adapter);
+  if (slice < 0 || slice >= p->n_slices) return fail(LORA_E_ARG, "slice %d out of range", slice);
+  const Slot& sl = p->slot(slice, adapter);
+  if (!sl.rank) return fail(LORA_E_NOT_RESIDENT, "adapter %d slice %d is not resident", adapter, slice);
+  if (a_scale) memcpy(a_scale, sl.qs.data(), sizeof(float) * (size_t)sl.rank);
+  if (b_scale) memcpy(b_scale, sl.qs.data() + sl.rank, sizeof(float) * (size_t)sl.rank);
   return LORA_OK;
 }
 

@@ -14,6 +14,7 @@ struct Slot {
   int32_t rs = 0;
   float scale = 0.f;
   std::vector<int32_t> pages;  // rank*npa A pages, then npb B pages
+  std::vector<float> qs;       // FP8 pools: a_scale [rank], then b_scale [rank]
 };
 
 lora_status fail(lora_status st, const char* fmt, ...);
@@ -29,9 +30,14 @@ lora_status scratch_init(int device);
                                                hipGetErrorString(_e));                     \
   } while (0)
 
-inline int elt_bytes(int dtype) { return dtype == LORA_F32 ? 4 : 2; }
+inline int elt_bytes(int dtype) { return dtype == LORA_F32 ? 4 : (dtype == LORA_FP8_E4M3 ? 1 : 2); }
 inline uint32_t nan_pattern(int dtype) {
-  return dtype == LORA_F32 ? 0x7FC00000u : (dtype == LORA_F16 ? 0x7E00u : 0x7FC0u);
+  switch (dtype) {
+    case LORA_F32: return 0x7FC00000u;
+    case LORA_F16: return 0x7E00u;
+    case LORA_FP8_E4M3: return 0x7Fu;
+    default: return 0x7FC0u;
+  }
 }
 
 }  // namespace lora
@@ -39,6 +45,7 @@ inline uint32_t nan_pattern(int dtype) {
 struct lora_pool {
   int32_t P = 0;
   int32_t dtype = 0;
+  int32_t act = 0;                 // activation dtype of x (16-bit y)
   int64_t n_pages = 0;
   int32_t max_adapters = 0;
   int32_t max_rank = 0;
@@ -56,7 +63,8 @@ struct lora_pool {
   bool dirty = true;
   uint64_t generation = 0;         // bumped by every residency change
   lora::DevEntry* d_entries = nullptr;
-  int32_t* d_page_ids = nullptr;
+  int32_t* d_page_ids = nullptr;   // page ids (and FP8 scales) of every resident slice
+  size_t page_ids_cap = 0;         // int32 words
   char* h_stage = nullptr;
   size_t h_stage_cap = 0;
   char* d_stage = nullptr;
@@ -67,6 +75,8 @@ struct lora_pool {
   const lora::Slot& slot(int slice, int adapter) const {
     return slots[(size_t)slice * max_adapters + adapter];
   }
+  bool quant() const { return dtype == LORA_FP8_E4M3; }
+  lora::Types types(int y_dtype) const { return lora::Types{dtype, act, y_dtype}; }
   int rs_of(int rank) const {
     const int per16 = 16 / elt;
     return (rank + per16 - 1) / per16 * per16;

@@ -13,9 +13,10 @@ import numpy as np
 
 from . import (LORA_POOL_HOST_ONLY, LORA_POOL_POISON, DTYPE_CODE, lora_page_table_build,
                lora_plan_prepare, lora_pool_alloc_pages, lora_pool_create, lora_pool_destroy,
-               lora_pool_upload, lora_workspace_size)
+               lora_pool_upload, lora_pool_upload_scaled, lora_workspace_size)
 
 _TORCH_DT = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+_ELT = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
 
 
 def torch_dtype(dtype: str):
@@ -28,6 +29,8 @@ def to_device(bits: np.ndarray, dtype: str, device="cuda"):
     a = np.ascontiguousarray(bits)
     if dtype == "f32":
         t = torch.from_numpy(a.astype(np.float32, copy=False))
+    elif dtype == "e4m3":
+        t = torch.from_numpy(a.view(np.uint8))
     else:
         t = torch.from_numpy(a.view(np.int16)).view(torch_dtype(dtype))
     return t.to(device)
@@ -38,6 +41,8 @@ def from_device(t, dtype: str) -> np.ndarray:
     c = t.detach().contiguous().cpu()
     if dtype == "f32":
         return c.to(torch.float32).numpy()
+    if dtype == "e4m3":
+        return c.view(torch.uint8).numpy()
     return c.view(torch.int16).numpy().view(np.uint16)
 
 
@@ -70,7 +75,7 @@ class SyntheticPool:
         ratio = wl.kv_dummy_ratio if kv_dummy is None else kv_dummy
         if n_pages is None:
             # exact page count of the uploaded subset
-            per16 = 16 // (4 if wl.dtype == "f32" else 2)
+            per16 = 16 // _ELT[wl.dtype]
             need = 0
             for a in adapters:
                 r = int(wl.ranks[a])
@@ -81,8 +86,10 @@ class SyntheticPool:
         self.n_pages = n_pages
         self.max_rank = max_rank or wl.max_rank
         flags = (LORA_POOL_POISON if poison else 0) | (LORA_POOL_HOST_ONLY if host_only else 0)
+        self.act = DTYPE_CODE[wl.act_dtype]
         self.handle = lora_pool_create(self.P, self.dt, n_pages, wl.n_adapters, self.max_rank,
-                                       wl.slices, shuffle_seed=wl.shuffle_seed, flags=flags)
+                                       wl.slices, shuffle_seed=wl.shuffle_seed, flags=flags,
+                                       act_dtype=self.act)
         self.kv_pages = []
         carry = 0.0
         for a in adapters:
@@ -90,9 +97,14 @@ class SyntheticPool:
             for s in range(len(wl.slices)):
                 A, B = wl.weights(a, s)
                 r = int(wl.ranks[a])
-                lora_pool_upload(self.handle, a, s, r, float(wl.scales[a]), A, B)
+                q = wl.qscales(a, s)
+                if q is None:
+                    lora_pool_upload(self.handle, a, s, r, float(wl.scales[a]), A, B)
+                else:
+                    lora_pool_upload_scaled(self.handle, a, s, r, float(wl.scales[a]), A, q[0], B,
+                                            q[1])
                 d_in, d_out = wl.slices[s]
-                per16 = 16 // (4 if wl.dtype == "f32" else 2)
+                per16 = 16 // _ELT[wl.dtype]
                 rs = -(-r // per16) * per16
                 used += r * -(-d_in // self.P) + -(-d_out // (self.P // rs))
             if ratio > 0:

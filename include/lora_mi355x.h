@@ -28,9 +28,10 @@
  *     (lora_bgmv_*, lora_sgmv_*, lora_apply) are stream-ordered: they neither
  *     allocate memory nor wait for the device.  Set-up calls (pool creation,
  *     upload, evict, page-table build, plan create/build/prepare) may do both.
- *   - x rows are d_in elements of the pool dtype, y rows d_out elements of
- *     y_dtype (the pool dtype or LORA_F32), both dense row-major, 16-byte
- *     aligned base pointers.  v (the shrink output) is fp32 [n][v_ld].
+ *   - x rows are d_in elements of the pool's activation dtype (act_dtype:
+ *     the page dtype, except 16-bit activations on FP8 pools), y rows d_out
+ *     elements of y_dtype (act_dtype or LORA_F32), both dense row-major,
+ *     16-byte aligned base pointers.  v (the shrink output) is fp32 [n][v_ld].
  *   - Adapter ids on the device should lie in [-1, max_adapters) and name
  *     adapters resident in the slice used.  The kernels treat any id outside
  *     [0, max_adapters) like -1 (the token is skipped) and a non-resident
@@ -47,7 +48,12 @@
 extern "C" {
 #endif
 
-typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
+/* LORA_FP8_E4M3: OCP 8-bit float codes (sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities) for quantised adapter pages, with fp32 scales
+ * per rank: A = diag(a_scale) A_codes, B = B_codes diag(b_scale) (the FP8
+ * adapters of the serving article's trade-offs section, which halve the bytes
+ * that uploads and gathers move). */
+typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2, LORA_FP8_E4M3 = 3 } lora_dtype;
 
 typedef enum {
   LORA_OK = 0,
@@ -81,7 +87,7 @@ typedef struct lora_plan lora_plan; /* opaque, library-owned */
  *
  * Layout of one uploaded adapter slice (rank r, dims d_in x d_out):
  *   r_s = r rounded up to a multiple of 16 bytes' worth of elements (4 for
- *         fp32, 8 for fp16/bf16)
+ *         fp32, 8 for fp16/bf16, 16 for FP8)
  *   A   : r rows of d_in elements; row k occupies ceil(d_in/P) pages, element j
  *         in page a_pages[k*ceil(d_in/P) + j/P] at position j % P.
  *   B   : d_out rows of r_s elements (columns r..r_s-1 are zero), packed
@@ -101,6 +107,9 @@ typedef struct {
   uint32_t flags;            /* LORA_POOL_* */
   void* pages_dev;           /* caller-owned device buffer of n_pages*P*elt bytes, or
                                 NULL: the library allocates (and frees) it            */
+  int32_t act_dtype;         /* lora_dtype of x (and of 16-bit y): equal to dtype for
+                                f32/f16/bf16 pools; LORA_F16 or LORA_BF16 for
+                                LORA_FP8_E4M3 pools (whose slices need d_in % 16 == 0) */
 } lora_pool_desc;
 
 lora_status lora_pool_create(const lora_pool_desc* desc, lora_pool** out);
@@ -119,10 +128,20 @@ lora_status lora_pool_free_pages(lora_pool* pool, int64_t n, const int32_t* page
  * dtype, scale stored as given (fp32).  The pages are taken from the free list
  * and written on `stream`; the call returns after the copies finish, so the host
  * buffers may be reused at once.  Uploading a resident slice is LORA_E_STATE.
- * Invalidates the device page table until lora_page_table_build. */
+ * Invalidates the device page table until lora_page_table_build.  FP8 pools
+ * take lora_pool_upload_scaled instead (LORA_E_ARG here). */
 lora_status lora_pool_upload(lora_pool* pool, int32_t adapter, int32_t slice, int32_t rank,
                              float scale, const void* A_host, const void* B_host,
                              void* stream);
+/* Upload of a quantised adapter slice to an FP8 pool: A_host [rank][d_in] and
+ * B_host [d_out][rank] FP8 E4M3 codes, a_scale_host [rank] (row k of A is
+ * a_scale[k] * codes) and b_scale_host [rank] (column k of B is codes *
+ * b_scale[k]), fp32.  Otherwise as lora_pool_upload; LORA_E_ARG on other
+ * pools or with a NULL scale array. */
+lora_status lora_pool_upload_scaled(lora_pool* pool, int32_t adapter, int32_t slice,
+                                    int32_t rank, float scale, const void* A_host,
+                                    const float* a_scale_host, const void* B_host,
+                                    const float* b_scale_host, void* stream);
 /* Return an adapter slice's pages to the free list (refilled with NaN under
  * LORA_POOL_POISON).  Evicting a non-resident slice is LORA_E_STATE. */
 lora_status lora_pool_evict(lora_pool* pool, int32_t adapter, int32_t slice, void* stream);
@@ -139,6 +158,11 @@ lora_status lora_pool_export_entry(const lora_pool* pool, int32_t adapter, int32
                                    int32_t* rank, float* scale, int32_t* n_a_pages,
                                    int32_t* a_pages_host, int32_t* n_b_pages,
                                    int32_t* b_pages_host);
+/* Host copy of a quantised adapter slice's scales: a_scale [rank], b_scale
+ * [rank] (LORA_E_ARG on pools that are not FP8, LORA_E_NOT_RESIDENT if the
+ * slice is not uploaded). */
+lora_status lora_pool_export_scales(const lora_pool* pool, int32_t adapter, int32_t slice,
+                                    float* a_scale_host, float* b_scale_host);
 /* Copy pages [first, first+count) of the pool to host memory (synchronous). */
 lora_status lora_pool_read_pages(const lora_pool* pool, int64_t first, int64_t count,
                                  void* dst_host);
@@ -275,6 +299,12 @@ lora_status lora_debug_resolve(lora_pool* pool, int32_t slice, const int32_t* id
  * A [rank][d_in] and B [d_out][rank] (pool dtype). */
 lora_status lora_debug_gather(lora_pool* pool, int32_t slice, int32_t adapter, void* A_dev,
                               void* B_dev, void* stream);
+
+/* Decode n stored elements of `dtype` (src_dev, 16-byte aligned, n * element
+ * bytes a multiple of 16) to fp32 dst_dev with the decoder the compute kernels
+ * use. */
+lora_status lora_debug_decode(int32_t dtype, const void* src_dev, int64_t n, float* dst_dev,
+                              void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* lora_last_error(void);

@@ -23,17 +23,18 @@ static int g_launches = 0;
 hipError_t launch_fill_pages(char*, int64_t, const int32_t*, int64_t, uint32_t, int, hipStream_t) STUB()
 hipError_t launch_fill_all(char*, int64_t, uint32_t, int, hipStream_t) STUB()
 hipError_t launch_scatter_pages(char*, int64_t, const char*, const int32_t*, int64_t, hipStream_t) STUB()
-hipError_t launch_bgmv_shrink(int, const PoolView&, const IoDesc&, const int32_t*, int32_t, float*,
-                              int32_t, hipStream_t) STUB()
-hipError_t launch_bgmv_expand(int, int, const PoolView&, const IoDesc&, const float*, int32_t,
+hipError_t launch_bgmv_shrink(const Types&, const PoolView&, const IoDesc&, const int32_t*, int32_t,
+                              float*, int32_t, hipStream_t) STUB()
+hipError_t launch_bgmv_expand(const Types&, const PoolView&, const IoDesc&, const float*, int32_t,
                               const int32_t*, int32_t, const float*, hipStream_t) STUB()
-hipError_t launch_bgmv_apply(int, int, const PoolView&, const IoSet&, const int32_t*, int32_t,
+hipError_t launch_bgmv_apply(const Types&, const PoolView&, const IoSet&, const int32_t*, int32_t,
                              hipStream_t) STUB()
-hipError_t launch_sgmv_shrink(int, const PoolView&, const PlanView&, const IoDesc&, float*, int32_t,
-                              hipStream_t) STUB()
-hipError_t launch_sgmv_expand(int, int, const PoolView&, const PlanView&, const IoDesc&, const float*,
+hipError_t launch_sgmv_shrink(const Types&, const PoolView&, const PlanView&, const IoDesc&, float*,
                               int32_t, hipStream_t) STUB()
-hipError_t launch_apply(int, int, const PoolView&, const PlanView&, const IoSet&, hipStream_t) STUB()
+hipError_t launch_sgmv_expand(const Types&, const PoolView&, const PlanView&, const IoDesc&,
+                              const float*, int32_t, hipStream_t) STUB()
+hipError_t launch_apply(const Types&, const PoolView&, const PlanView&, const IoSet&, hipStream_t) STUB()
+hipError_t launch_debug_decode(int, const void*, int64_t, float*, hipStream_t) STUB()
 hipError_t launch_debug_resolve(const PoolView&, const IoDesc&, int32_t, int, const int32_t*, int32_t,
                                 int64_t*, int64_t*, hipStream_t) STUB()
 hipError_t launch_debug_gather(int, const PoolView&, const IoDesc&, int32_t, int32_t, void*, void*,
@@ -53,7 +54,7 @@ static int g_bad = 0;
     }                                                                \
   } while (0)
 
-static int elt_of(int dt) { return dt == LORA_F32 ? 4 : 2; }
+static int elt_of(int dt) { return dt == LORA_F32 ? 4 : (dt == LORA_FP8_E4M3 ? 1 : 2); }
 
 static void one_case(std::mt19937& rng, int dt, int P, int d_in, int d_out, int n_slices,
                      int n_adapters) {
@@ -72,6 +73,7 @@ static void one_case(std::mt19937& rng, int dt, int P, int d_in, int d_out, int 
   d.slice_d_out = dout.data();
   d.shuffle_seed = rng();
   d.flags = LORA_POOL_HOST_ONLY | LORA_POOL_POISON;
+  d.act_dtype = dt == LORA_FP8_E4M3 ? (int)(LORA_F16 + rng() % 2) : dt;
   lora_pool* pool = nullptr;
   CHECK(lora_pool_create(&d, &pool) == LORA_OK);
   if (!pool) return;
@@ -81,9 +83,14 @@ static void one_case(std::mt19937& rng, int dt, int P, int d_in, int d_out, int 
     std::vector<char> A((size_t)rank[a] * d_in * elt), B((size_t)d_out * rank[a] * elt);
     for (auto& c : A) c = (char)(rng() & 0x3f);
     for (auto& c : B) c = (char)(rng() & 0x3f);
+    std::vector<float> sa(rank[a], 0.25f), sb(rank[a], 2.0f);
     int up = 0;
     for (; up < n_slices; ++up) {
-      const lora_status st = lora_pool_upload(pool, a, up, rank[a], 0.5f, A.data(), B.data(), nullptr);
+      const lora_status st =
+          dt == LORA_FP8_E4M3
+              ? lora_pool_upload_scaled(pool, a, up, rank[a], 0.5f, A.data(), sa.data(), B.data(),
+                                        sb.data(), nullptr)
+              : lora_pool_upload(pool, a, up, rank[a], 0.5f, A.data(), B.data(), nullptr);
       CHECK(st == LORA_OK || st == LORA_E_NOMEM);
       if (st != LORA_OK) break;
     }
@@ -117,6 +124,11 @@ static void one_case(std::mt19937& rng, int dt, int P, int d_in, int d_out, int 
       for (int i = 0; i < nb; ++i) {
         CHECK(bp[i] >= 0 && bp[i] < d.n_pages && !seen[bp[i]]);
         if (bp[i] >= 0 && bp[i] < d.n_pages) seen[bp[i]] = 1;
+      }
+      if (dt == LORA_FP8_E4M3 && r > 0) {
+        std::vector<float> qa((size_t)r), qb((size_t)r);
+        CHECK(lora_pool_export_scales(pool, a, s, qa.data(), qb.data()) == LORA_OK);
+        for (int k = 0; k < r; ++k) CHECK(qa[k] == 0.25f && qb[k] == 2.0f);
       }
     }
   std::vector<char> img((size_t)d.n_pages * P * elt);
@@ -176,9 +188,9 @@ int main(int argc, char** argv) {
   const int trials = argc > 1 ? atoi(argv[1]) : 20;
   std::mt19937 rng(77);
   for (int t = 0; t < trials; ++t) {
-    const int dt = (int)(rng() % 3);
+    const int dt = (int)(rng() % 4);
     const int P = (dt == LORA_F32 ? 64 : 128) * (1 + (int)(rng() % 4));
-    const int d_in = 8 * (1 + (int)(rng() % 64));
+    const int d_in = (dt == LORA_FP8_E4M3 ? 16 : 8) * (1 + (int)(rng() % 64));
     const int d_out = 8 * (1 + (int)(rng() % 96));
     one_case(rng, dt, P, d_in, d_out, 1 + (int)(rng() % 3), 2 + (int)(rng() % 12));
   }

@@ -52,6 +52,7 @@ def _host_pool(wl, **kw):
     ("f32", 256, 256, [4, 8, 8, 16], 256),          # the tiny configuration's shapes
     ("bf16", 48, 40, [5, 3, 13], 32),              # d_in spans 2 pages, odd ranks, ragged B
     ("f16", 64, 104, [16, 1, 9], 64),
+    ("e4m3", 96, 72, [5, 16, 33], 64),             # one-byte codes: r_s = rank rounded to 16
 ])
 def test_host_pool_layout_walks_back_to_dense(cfg_args):
     dtype, d_in, d_out, ranks, P = cfg_args
@@ -64,7 +65,11 @@ def test_host_pool_layout_walks_back_to_dense(cfg_args):
             for a in range(len(ranks)):
                 r, sc, ap, bp = L.lora_pool_export_entry(sp.handle, a, s)
                 assert r == ranks[a] and np.float32(sc) == wl.scales[a]
-                per16 = 16 // (4 if dtype == "f32" else 2)
+                per16 = 16 // W.ELT_BYTES[dtype]
+                if dtype == "e4m3":  # the per-rank scales come back as uploaded
+                    sa, sb = L.lora_pool_export_scales(sp.handle, a, s, r)
+                    qa, qb = wl.qscales(a, s)
+                    assert sa.tobytes() == qa.tobytes() and sb.tobytes() == qb.tobytes()
                 rs = -(-r // per16) * per16
                 assert ap.size == r * -(-d_in // P) and bp.size == -(-d_out // (P // rs))
                 for pg in np.concatenate([ap, bp]).tolist():
@@ -320,3 +325,43 @@ def test_binding_checks_buffers_before_the_call():
         with pytest.raises(TypeError, match="dtype"):
             L.lora_bgmv_expand(sp.handle, 0, torch.zeros((n, 8), dtype=torch.float64), ids, y,
                                L.LORA_BF16)
+
+
+def test_fp8_pool_arguments():
+    # FP8 pages need 16-bit activations, d_in a multiple of 16 and scaled uploads
+    base = dict(page_elems=64, dtype=L.LORA_FP8_E4M3, n_pages=64, max_adapters=2, max_rank=16,
+                slice_dims=[(64, 40)], flags=L.LORA_POOL_HOST_ONLY)
+    for kw in (dict(act_dtype=L.LORA_FP8_E4M3), dict(act_dtype=L.LORA_F32),
+               dict(act_dtype=L.LORA_F16, slice_dims=[(72, 40)])):
+        args = dict(base)
+        args.update(kw)
+        with pytest.raises(L.LoraError) as e:
+            L.lora_pool_create(**args)
+        assert e.value.status == -1, kw
+    with pytest.raises(L.LoraError) as e:  # 16-bit pools keep x in the page dtype
+        L.lora_pool_create(64, L.LORA_BF16, 16, 2, 8, [(64, 64)], flags=L.LORA_POOL_HOST_ONLY,
+                           act_dtype=L.LORA_F16)
+    assert e.value.status == -1
+    h = L.lora_pool_create(**dict(base, act_dtype=L.LORA_BF16))
+    try:
+        A = np.zeros((4, 64), np.uint8)
+        B = np.zeros((40, 4), np.uint8)
+        with pytest.raises(L.LoraError) as e:
+            L.lora_pool_upload(h, 0, 0, 4, 1.0, A, B)
+        assert e.value.status == -1 and "scaled" in str(e.value)
+        L.lora_pool_upload_scaled(h, 0, 0, 4, 1.0, A, np.ones(4), B, np.full(4, 0.5))
+        sa, sb = L.lora_pool_export_scales(h, 0, 0, 4)
+        assert np.all(sa == 1.0) and np.all(sb == 0.5)
+        with pytest.raises(L.LoraError) as e:
+            L.lora_pool_export_scales(h, 1, 0, 4)
+        assert e.value.status == -3
+    finally:
+        L.lora_pool_destroy(h)
+    h = L.lora_pool_create(64, L.LORA_BF16, 16, 2, 8, [(64, 64)], flags=L.LORA_POOL_HOST_ONLY)
+    try:
+        with pytest.raises(L.LoraError) as e:
+            L.lora_pool_upload_scaled(h, 0, 0, 4, 1.0, np.zeros((4, 64), np.uint16), np.ones(4),
+                                      np.zeros((64, 4), np.uint16), np.ones(4))
+        assert e.value.status == -1
+    finally:
+        L.lora_pool_destroy(h)

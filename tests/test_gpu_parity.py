@@ -18,8 +18,8 @@ import workloads as W  # noqa: E402
 from gather_lora_matmul_amd.synthetic import (SyntheticPool, from_device, prepare_shapes,  # noqa: E402
                                               to_device)
 
-from gpu_helpers import (Guarded, compare, compare_v, exact_compare, ids_tensor, log,  # noqa: E402
-                         reference)
+from gpu_helpers import (Guarded, check_all, compare, exact_compare, ids_tensor, log,  # noqa: E402
+                         reference, run_bgmv, run_sgmv)
 
 _POOLS = {}
 
@@ -39,71 +39,6 @@ def _cleanup():
         p.close()
     _POOLS.clear()
     torch.cuda.synchronize()
-
-
-def run_bgmv(sp, batch, slices, y_dtype, mode, return_v=False):
-    """mode: 'split' (shrink -> expand per slice) or 'fused' (one multi-slice apply).
-    Returns {slice: y bits}, and with return_v also {slice: v} (split mode)."""
-    wl = sp.wl
-    ids = ids_tensor(batch.ids)
-    n = len(batch.ids)
-    xs = {s: to_device(batch.x[s], wl.dtype) for s in slices}
-    ys = {s: Guarded(batch.y0[s], y_dtype) for s in slices}
-    ydt = W.DTYPE_CODE[y_dtype]
-    vs = {}
-    if mode == "split":
-        v_ld = sp.max_rank
-        for s in slices:
-            v = Guarded(np.full((n, v_ld), np.nan, np.float32), "f32")
-            L.lora_bgmv_shrink(sp.handle, s, xs[s], ids, v.view, v_ld)
-            L.lora_bgmv_expand(sp.handle, s, v.view, ids, ys[s].view, ydt, v_ld=v_ld)
-            vs[s] = v
-    else:
-        L.lora_bgmv_apply(sp.handle, [(s, xs[s], ys[s].view) for s in slices], ids, ydt)
-    torch.cuda.synchronize()
-    out = {s: ys[s].host() for s in slices}
-    vh = {s: v.host() for s, v in vs.items()}
-    return (out, vh) if return_v else out
-
-
-def run_sgmv(sp, batch, slices, y_dtype, mode, l_long=0, return_v=False):
-    wl = sp.wl
-    n = len(batch.ids)
-    plan = L.lora_plan_create(sp.handle, max(1, n))
-    L.lora_plan_build(plan, batch.ids, l_long=l_long)
-    shapes = [[s] for s in slices] if mode == "split" else [list(slices)]
-    ws = prepare_shapes(plan, shapes)
-    xs = {s: to_device(batch.x[s], wl.dtype) for s in slices}
-    ys = {s: Guarded(batch.y0[s], y_dtype) for s in slices}
-    ydt = W.DTYPE_CODE[y_dtype]
-    vs = {}
-    if mode == "split":
-        v_ld = sp.max_rank
-        for s in slices:
-            v = Guarded(np.full((n, v_ld), np.nan, np.float32), "f32")
-            L.lora_sgmv_shrink(sp.handle, plan, s, xs[s], v.view, v_ld, workspace=ws)
-            L.lora_sgmv_expand(sp.handle, plan, s, v.view, ys[s].view, ydt, v_ld=v_ld)
-            vs[s] = v
-    else:
-        L.lora_apply(sp.handle, plan, [(s, xs[s], ys[s].view) for s in slices], ydt, workspace=ws)
-    torch.cuda.synchronize()
-    stats = L.lora_plan_get_stats(plan)
-    L.lora_plan_destroy(plan)
-    out = {s: ys[s].host() for s in slices}
-    vh = {s: v.host() for s, v in vs.items()}
-    return (out, stats, vh) if return_v else (out, stats)
-
-
-def check_all(wl, b, ys, vs, slices, y_dtype, label):
-    """Every row of every slice against the oracle; v too when the split calls
-    produced it; the LoRA delta itself when y is fp32 on a non-zero y0."""
-    for s in slices:
-        if s in vs:
-            y_ref, v_ref = reference(wl, b, s, y_dtype, return_v=True)
-            compare_v(vs[s], v_ref, b.ids, wl.ranks, "%s s%d" % (label, s))
-        else:
-            y_ref = reference(wl, b, s, y_dtype)
-        compare(ys[s], y_ref, y_dtype, "%s s%d" % (label, s), y0_bits=b.y0[s])
 
 
 # ---------------------------------------------------------------------------
