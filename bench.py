@@ -291,6 +291,81 @@ def bandwidth_ceiling():
             "bytes": 4 * n, "kernels": "torch copy_ and sum over 1 GiB fp32, 10 calls each"}
 
 
+def residency(n_set: int = 64, steps: int = 100):
+    """On-demand residency on the Llama-7B decode shapes (4 slices, rank 16,
+    fp16): a host store of 4 * n_set + 1 adapters, a pool with room for all of
+    them; set A is resident and computed on, sets B1..B3 are loaded cold.
+    Reports the upload rate of a cold set, the time until one rare adapter is
+    usable, and how much of a load hides under compute already enqueued:
+    overlap = (t_compute + t_upload - t_both) / min(t_compute, t_upload)."""
+    import torch
+
+    import gather_lora_matmul_amd as L
+    import workloads as W
+    from gather_lora_matmul_amd.synthetic import to_device
+    wl = W.make_workload(1)
+    n_ad = 4 * n_set + 1
+    P = wl.page_elems
+    per_adapter = sum(16 + -(-d_out // (P // 16)) for _, d_out in wl.slices)
+    pool = L.lora_pool_create(P, L.LORA_F16, per_adapter * n_ad + 8, wl.n_adapters, 16, wl.slices,
+                              shuffle_seed=wl.shuffle_seed, act_dtype=L.LORA_F16)
+    L.lora_page_table_build(pool)
+    store = L.lora_store_create(pool)
+    t0 = time.perf_counter()
+    for a in range(n_ad):
+        for s in range(4):
+            A, B = wl.weights(a, s)
+            L.lora_store_add(store, a, s, 16, float(wl.scales[a]), A, B)
+    reg_s = time.perf_counter() - t0
+    up = torch.cuda.Stream()
+    cs = torch.cuda.current_stream()
+    sets = [np.arange(k * n_set, (k + 1) * n_set, dtype=np.int32) for k in range(4)]
+    L.lora_store_ensure(store, sets[0], upload_stream=up, compute_stream=cs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    ids = torch.from_numpy(rng.choice(sets[0], size=64).astype(np.int32)).cuda()
+    xs = [to_device(W.make_batch(wl, 0).x[s], "f16") for s in range(4)]
+    ys = [torch.zeros((64, 4096), dtype=torch.float16, device="cuda") for _ in range(4)]
+    call = L.prepare_bgmv_apply(pool, [(s, xs[s], ys[s]) for s in range(4)], ids, L.LORA_F16)
+    sh = cs.cuda_stream
+    for _ in range(10):
+        call(sh)
+    torch.cuda.synchronize()
+
+    def compute():
+        for _ in range(steps):
+            call(sh)
+
+    t = time.perf_counter()
+    compute()
+    torch.cuda.synchronize()
+    t_c = time.perf_counter() - t
+    bytes0 = L.lora_store_get_stats(store)["bytes_uploaded"]
+    t = time.perf_counter()
+    L.lora_store_ensure(store, sets[1], upload_stream=up, compute_stream=cs)
+    torch.cuda.synchronize()
+    t_u = time.perf_counter() - t
+    set_bytes = L.lora_store_get_stats(store)["bytes_uploaded"] - bytes0
+    t = time.perf_counter()
+    compute()
+    L.lora_store_ensure(store, sets[2], upload_stream=up, compute_stream=cs)
+    torch.cuda.synchronize()
+    t_both = time.perf_counter() - t
+    t = time.perf_counter()
+    L.lora_store_ensure(store, np.array([4 * n_set], np.int32), upload_stream=up, compute_stream=cs)
+    torch.cuda.synchronize()
+    t_one = time.perf_counter() - t
+    st = L.lora_store_get_stats(store)
+    L.lora_store_destroy(store)
+    L.lora_pool_destroy(pool)
+    return {"workload": "llama7b_decode_bgmv adapters (4 slices x rank 16, fp16: 1 MiB each)",
+            "set_adapters": n_set, "set_MB": set_bytes / 1e6, "upload_GBs": set_bytes / t_u / 1e9,
+            "upload_ms": t_u * 1e3, "compute_ms": t_c * 1e3, "both_ms": t_both * 1e3,
+            "overlap": (t_c + t_u - t_both) / min(t_c, t_u),
+            "one_adapter_ms": t_one * 1e3, "register_s": reg_s, "uploads": st["uploads"],
+            "compute": "%d lora_bgmv_apply steps on resident adapters" % steps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +451,9 @@ def main():
                 key, extra[key]["event_us_per_step"], extra[key]["roofline"]["frac"]),
                 file=sys.stderr, flush=True)
         out["workloads"] = extra
+        out["residency"] = residency()
+        print("[bench] residency: %.1f GB/s upload, overlap %.2f" % (
+            out["residency"]["upload_GBs"], out["residency"]["overlap"]), file=sys.stderr, flush=True)
         out["bandwidth_ceiling"] = bandwidth_ceiling()
     print(json.dumps(out), flush=True)
 

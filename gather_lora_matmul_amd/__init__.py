@@ -37,7 +37,8 @@ EXPORTS = (
     "lora_bgmv_apply", "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
     "lora_plan_get_stats", "lora_plan_export", "lora_plan_prepare", "lora_workspace_size",
     "lora_sgmv_shrink", "lora_sgmv_expand", "lora_apply", "lora_apply_noalloc", "lora_debug_resolve",
-    "lora_debug_gather", "lora_debug_decode", "lora_last_error",
+    "lora_debug_gather", "lora_debug_decode", "lora_last_error", "lora_store_create",
+    "lora_store_destroy", "lora_store_add", "lora_store_ensure", "lora_store_get_stats",
 )
 
 
@@ -60,6 +61,12 @@ class PoolDesc(ctypes.Structure):
 class Io(ctypes.Structure):
     _fields_ = [("slice", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("x_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p)]
+
+
+class StoreStats(ctypes.Structure):
+    _fields_ = [("uploads", ctypes.c_int64), ("evictions", ctypes.c_int64),
+                ("bytes_uploaded", ctypes.c_int64), ("resident", ctypes.c_int32),
+                ("registered", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):
@@ -91,6 +98,11 @@ def _load() -> ctypes.CDLL:
         "lora_pool_upload_scaled": [V, I32, I32, I32, F, V, V, V, V, V],
         "lora_pool_export_scales": [V, I32, I32, V, V],
         "lora_debug_decode": [I32, V, I64, V, V],
+        "lora_store_create": [V, ctypes.POINTER(V)],
+        "lora_store_destroy": [V],
+        "lora_store_add": [V, I32, I32, I32, F, V, V, V, V],
+        "lora_store_ensure": [V, I32, V, V, V],
+        "lora_store_get_stats": [V, ctypes.POINTER(StoreStats)],
         "lora_pool_evict": [V, I32, I32, V],
         "lora_page_table_build": [V, V],
         "lora_pool_export_entry": [V, I32, I32, V, V, V, V, V, V],
@@ -307,6 +319,46 @@ def lora_pool_read_pages(pool: int, first: int, count: int, page_elems: int, dty
     out = np.empty(count * page_elems, {LORA_F32: np.float32, LORA_FP8_E4M3: np.uint8}.get(dtype, np.uint16))
     _check(_lib.lora_pool_read_pages(pool, first, count, _np_ptr(out)), "lora_pool_read_pages")
     return out
+
+
+# ----------------------------------------------------------------------------
+# host adapter store
+# ----------------------------------------------------------------------------
+def lora_store_create(pool: int) -> int:
+    h = ctypes.c_void_p()
+    _check(_lib.lora_store_create(pool, ctypes.byref(h)), "lora_store_create")
+    return h.value
+
+
+def lora_store_destroy(store: int):
+    _check(_lib.lora_store_destroy(store), "lora_store_destroy")
+
+
+def lora_store_add(store: int, adapter: int, slice_: int, rank: int, scale: float,
+                   A_host: np.ndarray, B_host: np.ndarray, a_scale=None, b_scale=None):
+    A = np.ascontiguousarray(A_host)
+    B = np.ascontiguousarray(B_host)
+    sa = None if a_scale is None else np.ascontiguousarray(a_scale, np.float32)
+    sb = None if b_scale is None else np.ascontiguousarray(b_scale, np.float32)
+    _check(_lib.lora_store_add(store, adapter, slice_, rank, float(scale), _np_ptr(A),
+                               None if sa is None else _np_ptr(sa), _np_ptr(B),
+                               None if sb is None else _np_ptr(sb)), "lora_store_add")
+
+
+def lora_store_ensure(store: int, adapters: np.ndarray, upload_stream=None, compute_stream=None):
+    """upload_stream / compute_stream: raw hipStream_t ints or torch streams
+    (None: torch's current stream)."""
+    ids = np.ascontiguousarray(adapters, np.int32)
+    up = upload_stream if isinstance(upload_stream, int) else _stream(upload_stream)
+    cs = compute_stream if isinstance(compute_stream, int) else _stream(compute_stream)
+    _check(_lib.lora_store_ensure(store, ids.size, _np_ptr(ids) if ids.size else None, up, cs),
+           "lora_store_ensure")
+
+
+def lora_store_get_stats(store: int) -> dict:
+    st = StoreStats()
+    _check(_lib.lora_store_get_stats(store, ctypes.byref(st)), "lora_store_get_stats")
+    return {f: getattr(st, f) for f, _ in StoreStats._fields_}
 
 
 # ----------------------------------------------------------------------------

@@ -78,6 +78,122 @@ static lora_status ensure_dev_stage(lora_pool* p, size_t bytes) {
   return LORA_OK;
 }
 
+int64_t pages_of(const lora_pool* p, int slice, int rank) {
+  return (int64_t)rank * p->npa[(size_t)slice] + p->npb_of(slice, rank);
+}
+
+void pack_slice(const lora_pool* p, int slice, int rank, const void* A, const void* B, char* dst) {
+  const int d_in = p->d_in[(size_t)slice], d_out = p->d_out[(size_t)slice], npa = p->npa[(size_t)slice];
+  const int rs = p->rs_of(rank), rpp = p->P / rs;
+  const size_t data_bytes = (size_t)(pages_of(p, slice, rank) * p->page_bytes);
+  // page tails (and A pages past d_in) keep the pool's fill: NaN when poisoned
+  if (p->flags & LORA_POOL_POISON) fill_pattern(dst, data_bytes, nan_pattern(p->dtype), p->elt);
+  else memset(dst, 0, data_bytes);
+  const int elt = p->elt;
+  const char* Ab = (const char*)A;
+  const char* Bb = (const char*)B;
+  for (int k = 0; k < rank; ++k)
+    for (int c = 0; c < npa; ++c) {
+      const int j0 = c * p->P, j1 = std::min(d_in, j0 + p->P);
+      memcpy(dst + ((int64_t)k * npa + c) * p->page_bytes, Ab + ((int64_t)k * d_in + j0) * elt,
+             (size_t)(j1 - j0) * elt);
+    }
+  char* bstg = dst + (int64_t)rank * npa * p->page_bytes;
+  for (int m = 0; m < d_out; ++m) {
+    char* row = bstg + (int64_t)(m / rpp) * p->page_bytes + (int64_t)(m % rpp) * rs * elt;
+    memcpy(row, Bb + (int64_t)m * rank * elt, (size_t)rank * elt);
+    memset(row + (size_t)rank * elt, 0, (size_t)(rs - rank) * elt);
+  }
+}
+
+void reclaim_pages(lora_pool* p) {
+  if (p->host_only) return;
+  size_t keep = 0;
+  for (size_t i = 0; i < p->quarantine.size(); ++i) {
+    Quarantine& q = p->quarantine[i];
+    if (hipEventQuery(q.ev) == hipSuccess) {
+      for (int32_t pg : q.pages) {
+        p->state[(size_t)pg] = 0;
+        p->free_list.push_back(pg);
+      }
+      (void)hipEventDestroy(q.ev);
+    } else {
+      p->quarantine[keep++] = std::move(q);
+    }
+  }
+  p->quarantine.resize(keep);
+}
+
+lora_status publish_table(lora_pool* p, hipStream_t upload, hipStream_t compute) {
+  std::vector<DevEntry> ent(p->slots.size());
+  std::vector<int32_t> ids;
+  ids.reserve((size_t)p->n_pages);
+  for (int s = 0; s < p->n_slices; ++s)
+    for (int a = 0; a < p->max_adapters; ++a) {
+      const Slot& sl = p->slot(s, a);
+      DevEntry& e = ent[(size_t)s * p->max_adapters + a];
+      memset(&e, 0, sizeof(e));
+      if (!sl.rank) continue;
+      e.rank = sl.rank;
+      e.rs = sl.rs;
+      e.scale = sl.scale;
+      e.rpp = p->P / sl.rs;
+      e.inv_rpp = 1.0f / (float)e.rpp;
+      e.a_off = (int32_t)ids.size();
+      e.b_off = e.a_off + sl.rank * p->npa[s];
+      ids.insert(ids.end(), sl.pages.begin(), sl.pages.end());
+      if (p->quant()) {  // a_scale, then b_scale, as float bits
+        e.q_off = (int32_t)ids.size();
+        for (float f : sl.qs) {
+          int32_t w;
+          memcpy(&w, &f, 4);
+          ids.push_back(w);
+        }
+      }
+    }
+  if (p->host_only) {
+    p->dirty = false;
+    return LORA_OK;
+  }
+  if (ids.size() > p->page_ids_cap)
+    return fail(LORA_E_STATE, "page table of %zu words exceeds its %zu", ids.size(), p->page_ids_cap);
+  DevTable& t = p->tables[1 - p->cur];
+  const size_t eb = sizeof(DevEntry) * ent.size();
+  const size_t ib = sizeof(int32_t) * ids.size();
+  const size_t ioff = (eb + 255) & ~(size_t)255;
+  if (t.staged_pending) {  // the last copy out of this staging buffer
+    LORA_HIP(hipEventSynchronize(t.staged));
+    t.staged_pending = false;
+  }
+  if (t.h_cap < ioff + ib) {
+    if (t.h_stage) (void)hipHostFree(t.h_stage);
+    t.h_stage = nullptr;
+    t.h_cap = 0;
+    const size_t cap = ioff + ib + (ioff + ib) / 4 + 4096;
+    LORA_HIP(hipHostMalloc((void**)&t.h_stage, cap, hipHostMallocDefault));
+    t.h_cap = cap;
+  }
+  memcpy(t.h_stage, ent.data(), eb);
+  if (ib) memcpy(t.h_stage + ioff, ids.data(), ib);
+  // launches that read this buffer before it became inactive must be done
+  if (t.retired_pending) LORA_HIP(hipStreamWaitEvent(upload, t.retired, 0));
+  LORA_HIP(hipMemcpyAsync(t.entries, t.h_stage, eb, hipMemcpyHostToDevice, upload));
+  if (ib) LORA_HIP(hipMemcpyAsync(t.page_ids, t.h_stage + ioff, ib, hipMemcpyHostToDevice, upload));
+  LORA_HIP(hipEventRecord(t.staged, upload));
+  t.staged_pending = true;
+  if (compute != upload) {
+    LORA_HIP(hipEventRecord(p->pub_ev, upload));
+    LORA_HIP(hipStreamWaitEvent(compute, p->pub_ev, 0));
+  }
+  // launches enqueued on `compute` so far read the current buffer
+  DevTable& old = p->tables[p->cur];
+  LORA_HIP(hipEventRecord(old.retired, compute));
+  old.retired_pending = true;
+  p->cur = 1 - p->cur;
+  p->dirty = false;
+  return LORA_OK;
+}
+
 }  // namespace lora
 
 using namespace lora;
@@ -194,10 +310,15 @@ lora_status lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
   }
   // page ids of every page, plus (FP8) 2 * max_rank scale words per slot
   p->page_ids_cap = (size_t)p->n_pages + (quant ? 2 * (size_t)p->max_rank * p->slots.size() : 0);
-  e = hipMalloc((void**)&p->d_entries, sizeof(DevEntry) * p->slots.size());
-  if (e == hipSuccess) e = hipMalloc((void**)&p->d_page_ids, sizeof(int32_t) * p->page_ids_cap);
+  e = hipEventCreateWithFlags(&p->pub_ev, hipEventDisableTiming);
+  for (DevTable& t : p->tables) {
+    if (e == hipSuccess) e = hipMalloc((void**)&t.entries, sizeof(DevEntry) * p->slots.size());
+    if (e == hipSuccess) e = hipMalloc((void**)&t.page_ids, sizeof(int32_t) * p->page_ids_cap);
+    if (e == hipSuccess) e = hipMemset(t.entries, 0, sizeof(DevEntry) * p->slots.size());
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&t.staged, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&t.retired, hipEventDisableTiming);
+  }
   if (e == hipSuccess && poison) e = launch_fill_all(p->pages, bytes, nan_pattern(p->dtype), elt, nullptr);
-  if (e == hipSuccess) e = hipMemset(p->d_entries, 0, sizeof(DevEntry) * p->slots.size());
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     lora_pool_destroy(p);
@@ -216,8 +337,16 @@ lora_status lora_pool_destroy(lora_pool* p) {
   } else {
     (void)hipDeviceSynchronize();
     if (p->owns_pages && p->pages) (void)hipFree(p->pages);
-    if (p->d_entries) (void)hipFree(p->d_entries);
-    if (p->d_page_ids) (void)hipFree(p->d_page_ids);
+    for (DevTable& t : p->tables) {
+      if (t.entries) (void)hipFree(t.entries);
+      if (t.page_ids) (void)hipFree(t.page_ids);
+      if (t.h_stage) (void)hipHostFree(t.h_stage);
+      if (t.staged) (void)hipEventDestroy(t.staged);
+      if (t.retired) (void)hipEventDestroy(t.retired);
+    }
+    for (Quarantine& q : p->quarantine)
+      if (q.ev) (void)hipEventDestroy(q.ev);
+    if (p->pub_ev) (void)hipEventDestroy(p->pub_ev);
     if (p->d_stage) (void)hipFree(p->d_stage);
     if (p->h_stage) (void)hipHostFree(p->h_stage);
   }
@@ -228,6 +357,7 @@ lora_status lora_pool_destroy(lora_pool* p) {
 lora_status lora_pool_info(const lora_pool* p, int64_t* free_pages, void** base) {
   clear_error();
   if (!p) return fail(LORA_E_ARG, "null pool");
+  reclaim_pages(const_cast<lora_pool*>(p));
   if (free_pages) *free_pages = (int64_t)p->free_list.size();
   if (base) *base = p->pages;
   return LORA_OK;
@@ -236,6 +366,7 @@ lora_status lora_pool_info(const lora_pool* p, int64_t* free_pages, void** base)
 lora_status lora_pool_alloc_pages(lora_pool* p, int64_t n, int32_t* ids) {
   clear_error();
   if (!p || (n > 0 && !ids) || n < 0) return fail(LORA_E_ARG, "bad argument");
+  reclaim_pages(p);
   if ((int64_t)p->free_list.size() < n)
     return fail(LORA_E_NOMEM, "%lld pages requested, %zu free", (long long)n, p->free_list.size());
   for (int64_t i = 0; i < n; ++i) {
@@ -278,9 +409,9 @@ static lora_status upload_impl(lora_pool* p, int32_t adapter, int32_t slice, int
   if (rank < 1 || rank > p->max_rank) return fail(LORA_E_RANK, "rank %d outside [1, %d]", rank, p->max_rank);
   Slot& sl = p->slot(slice, adapter);
   if (sl.rank) return fail(LORA_E_STATE, "adapter %d slice %d already resident", adapter, slice);
-  const int d_in = p->d_in[slice], d_out = p->d_out[slice], npa = p->npa[slice];
-  const int rs = p->rs_of(rank), rpp = p->P / rs, npb = p->npb_of(slice, rank);
-  const int64_t need = (int64_t)rank * npa + npb;
+  reclaim_pages(p);
+  const int rs = p->rs_of(rank);
+  const int64_t need = pages_of(p, slice, rank);
   if ((int64_t)p->free_list.size() < need)
     return fail(LORA_E_NOMEM, "adapter %d slice %d needs %lld pages, %zu free", adapter, slice,
                 (long long)need, p->free_list.size());
@@ -288,26 +419,8 @@ static lora_status upload_impl(lora_pool* p, int32_t adapter, int32_t slice, int
   const size_t ids_off = (data_bytes + 255) & ~(size_t)255;
   lora_status st = ensure_host_stage(p, ids_off + sizeof(int32_t) * (size_t)need);
   if (st) return st;
-  // pack the page images
-  const bool poison = (p->flags & LORA_POOL_POISON) != 0;
   char* stg = p->h_stage;
-  if (poison) fill_pattern(stg, data_bytes, nan_pattern(p->dtype), p->elt);
-  else memset(stg, 0, data_bytes);
-  const int elt = p->elt;
-  const char* Ab = (const char*)A;
-  const char* Bb = (const char*)B;
-  for (int k = 0; k < rank; ++k)
-    for (int c = 0; c < npa; ++c) {
-      const int j0 = c * p->P, j1 = std::min(d_in, j0 + p->P);
-      memcpy(stg + ((int64_t)k * npa + c) * p->page_bytes, Ab + ((int64_t)k * d_in + j0) * elt,
-             (size_t)(j1 - j0) * elt);
-    }
-  char* bstg = stg + (int64_t)rank * npa * p->page_bytes;
-  for (int m = 0; m < d_out; ++m) {
-    char* row = bstg + (int64_t)(m / rpp) * p->page_bytes + (int64_t)(m % rpp) * rs * elt;
-    memcpy(row, Bb + (int64_t)m * rank * elt, (size_t)rank * elt);
-    memset(row + (size_t)rank * elt, 0, (size_t)(rs - rank) * elt);
-  }
+  pack_slice(p, slice, rank, A, B, stg);
   // take the pages
   std::vector<int32_t> pages((size_t)need);
   for (int64_t i = 0; i < need; ++i) {
@@ -420,48 +533,10 @@ lora_status lora_pool_evict(lora_pool* p, int32_t adapter, int32_t slice, void* 
 lora_status lora_page_table_build(lora_pool* p, void* stream) {
   clear_error();
   if (!p) return fail(LORA_E_ARG, "null pool");
-  std::vector<DevEntry> ent(p->slots.size());
-  std::vector<int32_t> ids;
-  ids.reserve((size_t)p->n_pages);
-  for (int s = 0; s < p->n_slices; ++s)
-    for (int a = 0; a < p->max_adapters; ++a) {
-      const Slot& sl = p->slot(s, a);
-      DevEntry& e = ent[(size_t)s * p->max_adapters + a];
-      memset(&e, 0, sizeof(e));
-      if (!sl.rank) continue;
-      e.rank = sl.rank;
-      e.rs = sl.rs;
-      e.scale = sl.scale;
-      e.rpp = p->P / sl.rs;
-      e.inv_rpp = 1.0f / (float)e.rpp;
-      e.a_off = (int32_t)ids.size();
-      e.b_off = e.a_off + sl.rank * p->npa[s];
-      ids.insert(ids.end(), sl.pages.begin(), sl.pages.end());
-      if (p->quant()) {  // a_scale, then b_scale, as float bits
-        e.q_off = (int32_t)ids.size();
-        for (float f : sl.qs) {
-          int32_t w;
-          memcpy(&w, &f, 4);
-          ids.push_back(w);
-        }
-      }
-    }
-  if (!p->host_only && ids.size() > p->page_ids_cap)
-    return fail(LORA_E_STATE, "page table of %zu words exceeds its %zu", ids.size(), p->page_ids_cap);
-  if (!p->host_only) {
-    const size_t eb = sizeof(DevEntry) * ent.size();
-    const size_t ib = sizeof(int32_t) * ids.size();
-    const size_t ioff = (eb + 255) & ~(size_t)255;
-    lora_status st = ensure_host_stage(p, ioff + ib);
-    if (st) return st;
-    memcpy(p->h_stage, ent.data(), eb);
-    if (ib) memcpy(p->h_stage + ioff, ids.data(), ib);
-    hipStream_t s = (hipStream_t)stream;
-    LORA_HIP(hipMemcpyAsync(p->d_entries, p->h_stage, eb, hipMemcpyHostToDevice, s));
-    if (ib) LORA_HIP(hipMemcpyAsync(p->d_page_ids, p->h_stage + ioff, ib, hipMemcpyHostToDevice, s));
-    LORA_HIP(hipStreamSynchronize(s));
-  }
-  p->dirty = false;
+  hipStream_t s = (hipStream_t)stream;
+  lora_status st = publish_table(p, s, s);
+  if (st) return st;
+  if (!p->host_only) LORA_HIP(hipStreamSynchronize(s));
   return LORA_OK;
 }
 

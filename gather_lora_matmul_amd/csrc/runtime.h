@@ -9,6 +9,23 @@
 
 namespace lora {
 
+// One buffer of the device page table with its pinned staging.
+struct DevTable {
+  DevEntry* entries = nullptr;
+  int32_t* page_ids = nullptr;    // page ids (and FP8 scales) of every resident slice
+  char* h_stage = nullptr;        // pinned image of the table being written
+  size_t h_cap = 0;
+  hipEvent_t staged = nullptr;    // the copy from h_stage has completed
+  bool staged_pending = false;
+  hipEvent_t retired = nullptr;   // launches that read this table have completed
+  bool retired_pending = false;
+};
+
+struct Quarantine {
+  std::vector<int32_t> pages;
+  hipEvent_t ev = nullptr;        // completes once the pages may be handed out again
+};
+
 struct Slot {
   int32_t rank = 0;   // 0: not resident
   int32_t rs = 0;
@@ -62,9 +79,16 @@ struct lora_pool {
   std::vector<uint8_t> state;      // per page: 0 free, 1 adapter, 2 other user
   bool dirty = true;
   uint64_t generation = 0;         // bumped by every residency change
-  lora::DevEntry* d_entries = nullptr;
-  int32_t* d_page_ids = nullptr;   // page ids (and FP8 scales) of every resident slice
-  size_t page_ids_cap = 0;         // int32 words
+  // Device page table, double-buffered: launches read tables[cur]; a rebuild
+  // writes the other one, on a stream ordered after the launches that last
+  // read it, and becomes current only for launches enqueued after it.
+  lora::DevTable tables[2];
+  int cur = 0;
+  hipEvent_t pub_ev = nullptr;     // a rebuilt table has been written
+  size_t page_ids_cap = 0;         // int32 words of each table's page-id list
+  // Pages of evicted slices waiting for the launches that may still read them
+  // (and their NaN refill) to finish before they return to the free list.
+  std::vector<lora::Quarantine> quarantine;
   char* h_stage = nullptr;
   size_t h_stage_cap = 0;
   char* d_stage = nullptr;
@@ -88,8 +112,8 @@ struct lora_pool {
   lora::PoolView view() const {
     lora::PoolView v;
     v.pages = pages;
-    v.entries = d_entries;
-    v.page_ids = d_page_ids;
+    v.entries = tables[cur].entries;
+    v.page_ids = tables[cur].page_ids;
     v.P = P;
     v.max_adapters = max_adapters;
     v.max_nch = rs_of(max_rank) * elt / 16;
@@ -107,6 +131,20 @@ struct lora_pool {
     return d;
   }
 };
+
+namespace lora {
+// Write the page table of the pool's current residency into the inactive
+// buffer on `upload` (after the launches that last read that buffer), make
+// `compute` wait for it and switch launches to it.  compute == upload for the
+// synchronous build.
+lora_status publish_table(lora_pool* p, hipStream_t upload, hipStream_t compute);
+// Return quarantined pages whose readers have finished to the free list.
+void reclaim_pages(lora_pool* p);
+// Page images of one adapter slice as the pool lays them out (rank * npa A
+// pages, then the B pages); dst holds pages_of(slice, rank) pages.
+void pack_slice(const lora_pool* p, int slice, int rank, const void* A, const void* B, char* dst);
+int64_t pages_of(const lora_pool* p, int slice, int rank);
+}  // namespace lora
 
 struct lora_plan;
 namespace lora {

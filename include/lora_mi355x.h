@@ -167,6 +167,51 @@ lora_status lora_pool_export_scales(const lora_pool* pool, int32_t adapter, int3
 lora_status lora_pool_read_pages(const lora_pool* pool, int64_t first, int64_t count,
                                  void* dst_host);
 
+/* ---------------------------------------------------------------------------
+ * Host adapter store and on-demand residency (S-LoRA explainer, "Unified
+ * Paging": every adapter lives in host memory and is paged into the pool when
+ * a request needs it, least recently used adapters leaving first; serving
+ * article, unified paged pool section: loads on dedicated streams overlapped
+ * with compute).
+ * ------------------------------------------------------------------------- */
+typedef struct lora_store lora_store; /* opaque, library-owned */
+typedef struct {
+  int64_t uploads;         /* adapter slices loaded into the pool */
+  int64_t evictions;       /* adapter slices evicted */
+  int64_t bytes_uploaded;  /* page bytes copied host -> device */
+  int32_t resident;        /* adapters resident in every slice */
+  int32_t registered;      /* adapters registered in every slice */
+} lora_store_stats;
+
+/* A store for a device pool.  The pool must outlive the store. */
+lora_status lora_store_create(lora_pool* pool, lora_store** out);
+lora_status lora_store_destroy(lora_store* store);
+/* Register one adapter slice (copied into pinned host memory as page images,
+ * so the host buffers may be reused at once).  Arguments as lora_pool_upload
+ * (a_scale/b_scale NULL) or, on FP8 pools, lora_pool_upload_scaled.  Nothing
+ * is loaded: the adapter becomes resident through lora_store_ensure. */
+lora_status lora_store_add(lora_store* store, int32_t adapter, int32_t slice, int32_t rank,
+                           float scale, const void* A_host, const float* a_scale_host,
+                           const void* B_host, const float* b_scale_host);
+/* Make the listed adapters (negative ids ignored) resident in every slice
+ * for the launches that follow.  Missing adapters are loaded on upload_stream
+ * (no host wait: work already enqueued on compute_stream keeps running); if the
+ * pool lacks free pages, store adapters outside the list are evicted, least
+ * recently used first, and their pages are overwritten only after
+ * compute_stream has passed this call (pages not reused are refilled with NaN
+ * under LORA_POOL_POISON and rejoin the free list when that is done).  A new
+ * page table is written into the inactive half of the pool's double-buffered
+ * table and compute_stream waits for it: launches enqueued on compute_stream
+ * after this call see the new residency, launches enqueued before it keep the
+ * table they were given.  Launches on other streams must be ordered by the
+ * caller.  Plans built before a call that changed residency are refused
+ * (rebuild them).  Host waits: only for the previous call's copies.  Errors:
+ * LORA_E_NOT_RESIDENT (an adapter not in the store), LORA_E_NOMEM (the list
+ * does not fit the pool), with the pool unchanged. */
+lora_status lora_store_ensure(lora_store* store, int32_t n, const int32_t* adapters_host,
+                              void* upload_stream, void* compute_stream);
+lora_status lora_store_get_stats(const lora_store* store, lora_store_stats* out);
+
 /* One adapted projection in a multi-slice launch: its slice index, its input
  * x [n][d_in] and its output y [n][d_out] (accumulated in place). */
 typedef struct {
