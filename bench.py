@@ -45,20 +45,20 @@ PLANNED_SOURCES = ("k_sgmv.hip", "kmfma.h", "kcommon.h", "kvalu.h", "lora_intern
                    "layout.cpp", "plan.cpp")
 
 
-def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int) -> int:
+def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int, shared_x: bool = False) -> int:
     """Bytes the method must move for one step: each distinct adapter's A and B
     once per slice (FP8 pages: one byte per code plus the 2 r fp32 scales), x
-    once, y read and written once."""
+    once (once for all slices when they read one x), y read and written once."""
     elt, elt_x = ELT[wl.dtype], ELT[wl.act_dtype]
     total = 0
     uniq = sorted(set(int(a) for a in ids.tolist() if a >= 0))
     n = len(ids)
-    for s in slices:
+    for j, s in enumerate(slices):
         d_in, d_out = wl.slices[s]
         for a in uniq:
             r = int(wl.ranks[a])
             total += r * (d_in + d_out) * elt + (8 * r if wl.quantized else 0)
-        total += n * d_in * elt_x + 2 * n * d_out * elt_y
+        total += (0 if shared_x and j > 0 else n * d_in * elt_x) + 2 * n * d_out * elt_y
     return total
 
 
@@ -137,7 +137,9 @@ class Runner:
     workspaces, and the step that applies one batch."""
 
     def __init__(self, name: str, mode: str = "fused", planned: bool = False, n_batches=None,
-                 l_long: int = 0):
+                 l_long: int = 0, qkv=None, n_tokens=None):
+        """qkv: None, or "separate" / "shared": q, k and v (slices 0-2) reading
+        one x buffer, without or with an x_group (decode BGMV only)."""
         import torch
 
         import gather_lora_matmul_amd as L
@@ -148,16 +150,23 @@ class Runner:
         self.wl = wl = W.make_workload(cfg)
         self.planned = planned or cfg in (3, 4)
         self.mode = mode
-        self.slices = slices = list(range(len(wl.slices)))
+        self.qkv = qkv
+        self.slices = slices = [0, 1, 2] if qkv else list(range(len(wl.slices)))
         n_batches = n_batches or (4 if self.planned else 16)
         t0 = time.perf_counter()
         print("[bench] %s: pool of %d adapters x %d slices" % (name, wl.n_adapters, len(slices)),
               file=sys.stderr, flush=True)
         self.sp = SyntheticPool(wl)
         self.setup_s = time.perf_counter() - t0
-        self.batches = [W.make_batch(wl, i) for i in range(n_batches)]
+        self.batches = [W.make_batch(wl, i, n_tokens=n_tokens) for i in range(n_batches)]
         self.ids_d = [torch.from_numpy(b.ids).cuda() for b in self.batches]
-        self.xs = [[to_device(b.x[s], wl.act_dtype) for s in slices] for b in self.batches]
+        if qkv:  # one x per batch for q, k and v
+            for b in self.batches:
+                b.x[1] = b.x[0]
+                b.x[2] = b.x[0]
+            self.xs = [[to_device(b.x[0], wl.act_dtype)] * 3 for b in self.batches]
+        else:
+            self.xs = [[to_device(b.x[s], wl.act_dtype) for s in slices] for b in self.batches]
         self.ys = [[to_device(b.y0[s], wl.act_dtype) for s in slices] for b in self.batches]
         self.ydt = W.DTYPE_CODE[wl.act_dtype]
         self.n = len(self.batches[0].ids)
@@ -185,7 +194,8 @@ class Runner:
         self.calls = []
         if mode == "fused":
             for k, b in enumerate(self.batches):
-                io = [(s, self.xs[k][j], self.ys[k][j]) for j, s in enumerate(slices)]
+                group = 1 if qkv == "shared" else 0
+                io = [(s, self.xs[k][j], self.ys[k][j], group) for j, s in enumerate(slices)]
                 self.calls.append(
                     L.prepare_apply(self.sp.handle, self.plans[k], io, self.ydt, workspace=self.wss[k])
                     if self.planned else L.prepare_bgmv_apply(self.sp.handle, io, self.ids_d[k], self.ydt))
@@ -236,7 +246,7 @@ class Runner:
         wall = time.perf_counter() - t0
         event_s = e0.elapsed_time(e1) * 1e-3 / steps
         used = [algorithmic_bytes(self.wl, self.batches[(warmup + i) % len(self.batches)].ids,
-                                  self.slices, 2) for i in range(steps)]
+                                  self.slices, 2, shared_x=bool(self.qkv)) for i in range(steps)]
         return wall, event_s, float(np.mean(used))
 
     def record(self, steps: int, warmup: int):
@@ -438,13 +448,21 @@ def main():
         extra = {}
         steps = min(args.steps, 50)
         warm = min(args.warmup, 5)
-        for name, planned in (("llama7b_decode_bgmv_fp8", False), ("hetero_decode_bgmv", False),
-                              ("hetero_decode_bgmv", True), ("llama13b_prefill_sgmv", True),
-                              ("llama70b_mixed_apply", True)):
+        for name, planned, qkv, ntok in (("llama7b_decode_bgmv", False, "separate", None),
+                                         ("llama7b_decode_bgmv", False, "shared", None),
+                                         ("llama7b_decode_bgmv", False, "separate", 256),
+                                         ("llama7b_decode_bgmv", False, "shared", 256),
+                                         ("llama7b_decode_bgmv_fp8", False, None, None),
+                                         ("hetero_decode_bgmv", False, None, None),
+                                         ("hetero_decode_bgmv", True, None, None),
+                                         ("llama13b_prefill_sgmv", True, None, None),
+                                         ("llama70b_mixed_apply", True, None, None)):
             key = name + ("/planned" if planned and WORKLOADS[name] in (1, 2) else "")
-            if name == args.workload and planned == head.planned:
+            key += "/qkv_%s_x" % qkv if qkv else ""
+            key += "_%dtok" % ntok if ntok else ""
+            if name == args.workload and planned == head.planned and not qkv:
                 continue
-            r = Runner(name, "fused", planned)
+            r = Runner(name, "fused", planned, qkv=qkv, n_tokens=ntok)
             extra[key] = r.record(steps, warm)
             r.close()
             print("[bench] %s: %.1f us per step, %.3f of 8 TB/s" % (

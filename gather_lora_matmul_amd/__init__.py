@@ -59,7 +59,7 @@ class PoolDesc(ctypes.Structure):
 
 
 class Io(ctypes.Structure):
-    _fields_ = [("slice", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("slice", ctypes.c_int32), ("x_group", ctypes.c_int32),
                 ("x_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p)]
 
 
@@ -187,7 +187,8 @@ def _check_ids(ids):
 
 def _check_io(pool: int, ios, n: int, y_dtype: int):
     info = _POOLS.get(pool)
-    for k, (s, x, y) in enumerate(ios):
+    for k, e in enumerate(ios):
+        s, x, y = e[:3]
         if info is None:
             continue
         dt, dims, _ = info
@@ -392,16 +393,18 @@ def lora_bgmv_expand(pool: int, slice_: int, v, ids, y, y_dtype: int, token_scal
            "lora_bgmv_expand")
 
 
-def _ios(ios: Sequence[Tuple[int, object, object]]):
+def _ios(ios):
+    """io entries (slice, x, y) or (slice, x, y, x_group) -> lora_io array."""
     arr = (Io * len(ios))()
-    for k, (s, x, y) in enumerate(ios):
-        arr[k] = Io(int(s), 0, _dev_ptr(x), _dev_ptr(y))
+    for k, e in enumerate(ios):
+        s, x, y = e[:3]
+        arr[k] = Io(int(s), int(e[3]) if len(e) > 3 else 0, _dev_ptr(x), _dev_ptr(y))
     return arr
 
 
 def lora_bgmv_apply(pool: int, ios: Sequence[Tuple[int, object, object]], ids, y_dtype: int,
                     stream=None):
-    """ios: [(slice, x, y), ...] sharing `ids`."""
+    """ios: [(slice, x, y) or (slice, x, y, x_group), ...] sharing `ids`."""
     _check_ids(ids)
     _check_io(pool, ios, int(ids.shape[0]), y_dtype)
     arr = _ios(ios)

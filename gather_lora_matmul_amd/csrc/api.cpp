@@ -45,18 +45,49 @@ lora_status hip_status(hipError_t e, const char* what) {
   return LORA_OK;
 }
 
-lora_status build_ioset(const lora_pool* p, int32_t n_io, const lora_io* io, IoSet& ios) {
+// The io entries of a call; with `groups`, entries sharing an x_group are
+// made contiguous and described by grp_start (n_groups stays 0 when no group
+// has two members).
+lora_status build_ioset(const lora_pool* p, int32_t n_io, const lora_io* io, IoSet& ios,
+                        bool groups = false) {
   if (n_io < 1 || n_io > LORA_MAX_IO || !io) return fail(LORA_E_ARG, "n_io must be in [1, %d]", LORA_MAX_IO);
   memset(&ios, 0, sizeof(ios));
   ios.n_io = n_io;
+  bool shared = false;
   for (int k = 0; k < n_io; ++k) {
     lora_status st = check_slice(p, io[k].slice);
     if (st) return st;
     if (!io[k].x_dev || !io[k].y_dev) return fail(LORA_E_ARG, "io %d: null x or y", k);
     if (!aligned16(io[k].x_dev) || !aligned16(io[k].y_dev)) return fail(LORA_E_ARG, "io %d: x/y not 16-byte aligned", k);
+    if (io[k].x_group < 0) return fail(LORA_E_ARG, "io %d: negative x_group", k);
+    for (int j = 0; j < k; ++j)
+      if (io[k].x_group && io[j].x_group == io[k].x_group) {
+        if (io[j].x_dev != io[k].x_dev || p->d_in[(size_t)io[j].slice] != p->d_in[(size_t)io[k].slice])
+          return fail(LORA_E_ARG, "io %d and %d: x_group %d needs one x and one d_in", j, k,
+                      io[k].x_group);
+        shared = true;
+      }
     ios.io[k] = p->io(io[k].slice, io[k].x_dev, io[k].y_dev);
     ios.max_d_in = std::max(ios.max_d_in, ios.io[k].d_in);
     ios.max_d_out = std::max(ios.max_d_out, ios.io[k].d_out);
+  }
+  if (groups && shared) {
+    // group members contiguous, groups in first-appearance order; an entry
+    // without a group is a group of its own
+    std::vector<char> taken((size_t)n_io, 0);
+    IoDesc ord[LORA_MAX_IO];
+    int m = 0;
+    for (int k = 0; k < n_io; ++k) {
+      if (taken[(size_t)k]) continue;
+      ios.grp_start[ios.n_groups++] = m;
+      for (int j = k; j < n_io; ++j)
+        if (!taken[(size_t)j] && (j == k || (io[k].x_group && io[j].x_group == io[k].x_group))) {
+          taken[(size_t)j] = 1;
+          ord[m++] = ios.io[j];
+        }
+    }
+    ios.grp_start[ios.n_groups] = m;
+    for (int k = 0; k < n_io; ++k) ios.io[k] = ord[k];
   }
   return LORA_OK;
 }
@@ -137,13 +168,14 @@ lora_status lora_bgmv_expand(lora_pool* p, int32_t slice, const float* v, int32_
 lora_status lora_bgmv_apply(lora_pool* p, int32_t n_io, const lora_io* io, const int32_t* ids,
                             int32_t n, int32_t y_dtype, void* stream) {
   clear_error();
-  LORA_TRY(check_pool(p));
+  if (!p) return fail(LORA_E_ARG, "null pool");
   LORA_TRY(check_ydt(p, y_dtype));
   IoSet ios;
-  LORA_TRY(build_ioset(p, n_io, io, ios));
+  LORA_TRY(build_ioset(p, n_io, io, ios, true));
   if (n < 0) return fail(LORA_E_ARG, "n < 0");
   if (n == 0) return LORA_OK;
   if (!ids) return fail(LORA_E_ARG, "null ids");
+  LORA_TRY(check_pool(p));
   return hip_status(launch_bgmv_apply(p->types(y_dtype), p->view(), ios, ids, n, (hipStream_t)stream),
                     "bgmv_apply");
 }

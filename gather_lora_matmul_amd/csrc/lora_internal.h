@@ -35,7 +35,7 @@ struct PoolView {
   int32_t P;                  // elements per page
   int32_t max_adapters;
   int32_t max_nch;            // 16-byte chunks in the longest stored B row of the pool
-  int32_t pad;
+  int32_t n_cu;               // compute units of the pool's device
 };
 
 // Per-slice input/output of one launch.
@@ -53,7 +53,10 @@ struct IoSet {
   int32_t n_io;
   int32_t max_d_out;
   int32_t max_d_in;
-  int32_t pad;
+  // Slices that share one x (lora_io.x_group): 0 = none; otherwise io is
+  // ordered by group and group g holds io[grp_start[g] .. grp_start[g + 1]).
+  int32_t n_groups;
+  int32_t grp_start[LORA_MAX_IO + 1];
 };
 
 // One unit of planned SGMV work: `count` tokens (perm[start .. start+count))

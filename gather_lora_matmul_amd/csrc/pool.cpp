@@ -281,9 +281,11 @@ lora_status lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
     return LORA_OK;
   }
   hipError_t e = hipGetDevice(&p->device);
-  if (e != hipSuccess) {
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&p->n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess || p->n_cu <= 0) {
     delete p;
-    return fail(LORA_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return fail(LORA_E_HIP, "device query: %s", hipGetErrorString(e));
   }
   if (d->pages_dev) {
     if ((uintptr_t)d->pages_dev % 256) {

@@ -94,6 +94,7 @@ struct lora_pool {
   char* d_stage = nullptr;
   size_t d_stage_cap = 0;
   int device = 0;
+  int32_t n_cu = 256;              // compute units of the device
 
   lora::Slot& slot(int slice, int adapter) { return slots[(size_t)slice * max_adapters + adapter]; }
   const lora::Slot& slot(int slice, int adapter) const {
@@ -117,7 +118,7 @@ struct lora_pool {
     v.P = P;
     v.max_adapters = max_adapters;
     v.max_nch = rs_of(max_rank) * elt / 16;
-    v.pad = 0;
+    v.n_cu = n_cu;
     return v;
   }
   lora::IoDesc io(int slice, const void* x, void* y) const {

@@ -213,10 +213,17 @@ lora_status lora_store_ensure(lora_store* store, int32_t n, const int32_t* adapt
 lora_status lora_store_get_stats(const lora_store* store, lora_store_stats* out);
 
 /* One adapted projection in a multi-slice launch: its slice index, its input
- * x [n][d_in] and its output y [n][d_out] (accumulated in place). */
+ * x [n][d_in] and its output y [n][d_out] (accumulated in place).  x_group:
+ * 0, or a positive id that entries reading one and the same x share (q, k and
+ * v of a layer, gate and up of an MLP): their x_dev and d_in must be equal
+ * (LORA_E_ARG otherwise).  When a batch has at least one (group, token) pair
+ * per compute unit, lora_bgmv_apply reads a token's x once and dots it
+ * against the A rows of every slice of the group in one block; smaller
+ * batches run one block per (slice, token), a token's blocks sharing one L2.
+ * The results are those of separate x, bit for bit. */
 typedef struct {
   int32_t slice;
-  int32_t reserved;
+  int32_t x_group;
   const void* x_dev;
   void* y_dev;
 } lora_io;
@@ -236,7 +243,9 @@ lora_status lora_bgmv_expand(lora_pool* pool, int32_t slice, const float* v_dev,
                              const int32_t* ids_dev, int32_t n, const float* token_scale_dev,
                              void* y_dev, int32_t y_dtype, void* stream);
 /* Fused shrink + expand in one launch for up to LORA_MAX_IO slices (v never
- * leaves the chip).  All io entries share ids and n. */
+ * leaves the chip).  All io entries share ids and n.  Entries with a common
+ * x_group may run as one block per (group, token) with x read once (see
+ * lora_io). */
 lora_status lora_bgmv_apply(lora_pool* pool, int32_t n_io, const lora_io* io_host,
                             const int32_t* ids_dev, int32_t n, int32_t y_dtype, void* stream);
 
@@ -310,7 +319,8 @@ lora_status lora_sgmv_expand(lora_pool* pool, const lora_plan* plan, int32_t sli
                              const float* v_dev, int32_t v_ld, void* y_dev, int32_t y_dtype,
                              void* stream);
 /* Fused shrink + expand for a planned (mixed prefill + decode) batch, for up to
- * LORA_MAX_IO slices; v is never materialized.  Short items: one launch, v in
+ * LORA_MAX_IO slices; v is never materialized.  x_group is checked as for
+ * lora_bgmv_apply; each slice's shrink reads x itself.  Short items: one launch, v in
  * LDS.  MFMA tiles: two launches on `stream` (shrink ranges keep partial tiles
  * in workspace_dev; the expand sums them while loading V).  The launch shape
  * (the io slices in this order) must be prepared; workspace_dev as for

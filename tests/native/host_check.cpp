@@ -166,9 +166,10 @@ static void one_case(std::mt19937& rng, int dt, int P, int d_in, int d_out, int 
     }
     // compute calls on a host-only pool: refused on the host, nothing launched
     lora_io bad[2] = {{0, 0, (void*)16, (void*)16}, {n_slices, 0, (void*)16, (void*)16}};
-    CHECK(lora_apply(pool, plan, 2, bad, dt, (void*)16, 1 << 30, nullptr) == LORA_E_ARG);
-    CHECK(lora_apply(pool, plan, 1, bad, dt, (void*)16, (size_t)1 << 30, nullptr) != LORA_OK);
-    CHECK(lora_bgmv_apply(pool, 1, bad, (const int32_t*)16, n, dt, nullptr) == LORA_E_STATE);
+    CHECK(lora_apply(pool, plan, 2, bad, d.act_dtype, (void*)16, 1 << 30, nullptr) == LORA_E_ARG);
+    CHECK(lora_apply(pool, plan, 1, bad, d.act_dtype, (void*)16, (size_t)1 << 30, nullptr) != LORA_OK);
+    CHECK(lora_bgmv_apply(pool, 1, bad, (const int32_t*)16, n, d.act_dtype, nullptr) == LORA_E_STATE);
+    CHECK(lora_bgmv_apply(pool, 2, bad, (const int32_t*)16, n, d.act_dtype, nullptr) == LORA_E_ARG);
     int32_t over = n_adapters;
     CHECK(lora_plan_build(plan, &over, 1, 0, nullptr) == LORA_E_ARG);
     CHECK(lora_plan_build(plan, ids.data(), n + 1, 0, nullptr) == LORA_E_ARG);

@@ -365,3 +365,21 @@ def test_fp8_pool_arguments():
         assert e.value.status == -1
     finally:
         L.lora_pool_destroy(h)
+
+
+def test_x_group_needs_one_x_and_one_d_in():
+    # entries of one x_group must name the same x buffer and d_in; the check
+    # comes before the pool's state (a host-only pool runs nothing)
+    wl = W.small_workload("bf16", 64, 64, [8], 64, n_slices=3)
+    wl.slices[2] = (128, 64)
+    with _host_pool(wl) as sp:
+        lib, a, b = L.lib(), 1 << 20, 2 << 20
+        io = (L.Io * 2)(L.Io(0, 1, a, a), L.Io(1, 1, b, b))
+        assert lib.lora_bgmv_apply(sp.handle, 2, io, a, 4, L.LORA_BF16, None) == -1
+        assert "x_group" in L.lora_last_error()
+        io = (L.Io * 2)(L.Io(0, 2, a, a), L.Io(2, 2, a, b))
+        assert lib.lora_bgmv_apply(sp.handle, 2, io, a, 4, L.LORA_BF16, None) == -1
+        io = (L.Io * 2)(L.Io(0, 1, a, a), L.Io(1, -3, a, b))
+        assert lib.lora_bgmv_apply(sp.handle, 2, io, a, 4, L.LORA_BF16, None) == -1
+        io = (L.Io * 3)(L.Io(0, 1, a, a), L.Io(2, 0, b, b), L.Io(1, 1, a, b))
+        assert lib.lora_bgmv_apply(sp.handle, 3, io, a, 4, L.LORA_BF16, None) == -5  # valid: pool state

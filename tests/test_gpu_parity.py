@@ -190,6 +190,52 @@ def test_bgmv_zero_token_scale():
     assert np.all(v.cpu().numpy()[b.ids < 0] == 0)
 
 
+@pytest.mark.parametrize("cfg", [1, 5])
+@pytest.mark.parametrize("n", [64, 256])
+def test_bgmv_shared_x_groups(cfg, n):
+    """q, k and v reading one x (x_group 1) and o its own: 256 tokens give one
+    block per (group, token) that reads x once, 64 tokens one block per
+    (slice, token); every row matches the oracle and the same buffers without
+    groups give the same bits."""
+    wl = W.make_workload(cfg)
+    act = wl.act_dtype
+    log("[case] shared-x groups cfg=%d n=%d" % (cfg, n))
+    sp = pool_for("cfg%d" % cfg, wl)
+    b = W.make_batch(wl, 2, n_tokens=n)
+    b.x[1] = b.x[0]
+    b.x[2] = b.x[0]
+    ids = ids_tensor(b.ids)
+    xs = [to_device(b.x[0], act)] * 3 + [to_device(b.x[3], act)]
+    out = {}
+    for grouped in (True, False):
+        ys = [Guarded(b.y0[s], act) for s in range(4)]
+        io = [(s, xs[s], ys[s].view, 1 if (grouped and s < 3) else 0) for s in range(4)]
+        L.lora_bgmv_apply(sp.handle, io, ids, W.DTYPE_CODE[act])
+        torch.cuda.synchronize()
+        out[grouped] = {s: ys[s].host() for s in range(4)}
+    check_all(wl, b, out[True], {}, [0, 1, 2, 3], act, "shared x cfg%d" % cfg)
+    for s in range(4):
+        assert out[True][s].tobytes() == out[False][s].tobytes(), "slice %d differs" % s
+
+
+def test_bgmv_shared_x_multi_page_rows():
+    # A rows over two pages take the general body inside a group (x read per
+    # slice there); results still match
+    wl = W.small_workload("bf16", 512, 264, [8, 40, 16], 256, n_slices=3, seed=12)
+    sp = pool_for(("shared_mp",), wl)
+    ids = np.array([0, 2, 1, -1, 2, 2, 0, 1] * 3, np.int32)
+    b = W.custom_batch(wl, ids, zero_y0=True)
+    b.x[1] = b.x[0]
+    log("[case] shared-x multi-page rows")
+    xs = [to_device(b.x[0], "bf16"), None, to_device(b.x[2], "bf16")]
+    xs[1] = xs[0]
+    ys = [Guarded(b.y0[s], "bf16") for s in range(3)]
+    L.lora_bgmv_apply(sp.handle, [(0, xs[0], ys[0].view, 7), (2, xs[2], ys[2].view, 0),
+                                  (1, xs[1], ys[1].view, 7)], ids_tensor(ids), L.LORA_BF16)
+    torch.cuda.synchronize()
+    check_all(wl, b, {s: ys[s].host() for s in range(3)}, {}, [0, 1, 2], "bf16", "shared x mp")
+
+
 def test_bgmv_deterministic_and_placement_independent():
     wl = W.make_workload(2)
     b = W.make_batch(wl, 3, n_tokens=64)
