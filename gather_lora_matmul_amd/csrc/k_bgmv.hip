@@ -428,9 +428,11 @@ hipError_t apply_t(const PoolView& pv, const IoSet& ios_in, const int32_t* ids, 
   const int units = n * ios.n_io;
   // Splitting a unit repeats its whole shrink, which costs more than it
   // gains (measured, also when only the units with the largest B are split);
-  // split only when there are fewer units than CUs.
+  // split only while the split units still run in one round of one block per
+  // compute unit: a second, partly filled round costs more than the compute
+  // units one round leaves idle (Llama-7B q/k/v at 64 tokens, 192 units).
   int nsplit = 1;
-  while ((long)units * nsplit < 256 && ios.max_d_out / (nsplit * 2) >= 512) nsplit *= 2;
+  while ((long)units * nsplit * 2 <= pv.n_cu && ios.max_d_out / (nsplit * 2) >= 512) nsplit *= 2;
   const int rps = (((ios.max_d_out + nsplit - 1) / nsplit) + 63) & ~63;
   const dim3 grid(xcd_grid(units, nsplit));
   const int C = ios.max_d_in / E;

@@ -236,6 +236,34 @@ def test_bgmv_shared_x_multi_page_rows():
     check_all(wl, b, {s: ys[s].host() for s in range(3)}, {}, [0, 1, 2], "bf16", "shared x mp")
 
 
+@pytest.mark.parametrize("n", [129, 500, 513])
+def test_bgmv_batch_independent_bits(n):
+    """Larger fused batches with repeated, skipped and out-of-table ids and n
+    not a multiple of 8 match the oracle, and every token's bits equal those of
+    the same token in a smaller batch (a token's result does not depend on
+    the batch around it or on the launch shape)."""
+    wl = W.make_workload(2)
+    sp = pool_for("cfg2", wl)
+    b = W.make_batch(wl, 4, zero_y0=False, n_tokens=n)
+    b.ids[::13] = -1
+    b.ids[5::17] = wl.n_adapters
+    b.ids[7] = 2 ** 31 - 1
+    b.ids[n // 2: n // 2 + 40] = b.ids[n // 2]  # a long run of one adapter
+    log("[case] batch-independent bits n=%d, %d distinct ids" % (n, len(set(b.ids.tolist()))))
+    ys = run_bgmv(sp, b, [0, 1], wl.dtype, "fused")
+    skip = (b.ids < 0) | (b.ids >= wl.n_adapters)
+    ref_b = W.Batch(ids=np.where(skip, -1, b.ids).astype(np.int32), x=b.x, y0=b.y0)
+    check_all(wl, ref_b, ys, {}, [0, 1], wl.dtype, "batch bits n=%d" % n)
+    step = 100
+    for lo in range(0, n, step):
+        hi = min(n, lo + step)
+        sub = W.Batch(ids=b.ids[lo:hi].copy(), x=[x[lo:hi] for x in b.x],
+                      y0=[y[lo:hi] for y in b.y0])
+        ysub = run_bgmv(sp, sub, [0, 1], wl.dtype, "fused")
+        for s in (0, 1):
+            assert ysub[s].tobytes() == ys[s][lo:hi].tobytes(), "tokens %d..%d slice %d" % (lo, hi, s)
+
+
 def test_bgmv_deterministic_and_placement_independent():
     wl = W.make_workload(2)
     b = W.make_batch(wl, 3, n_tokens=64)
