@@ -388,19 +388,51 @@ void apply_grouped_launch(const PoolView& pv, const IoSet& ios, const int32_t* i
     hipLaunchKernelGGL((k_bgmv_apply_grouped<T, X, TY, NT, U, kMaxN>), grid, dim3(NT), 0, s, pv, ios, ids, n);
 }
 
+// Blocks of `kernel` (NT threads) resident per compute unit, looked up once
+// per kernel; 1 if the query fails.
+inline int resident_blocks(const void* kernel, int nt) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, nt, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  return nb > 0 ? nb : 1;
+}
+
+// Splitting a unit repeats its whole shrink, which costs more than it gains
+// (measured, also when only the units with the largest B are split); split
+// only while the split units still run in one round of resident blocks: a
+// second, partly filled round costs more than the slots one round leaves idle
+// (Llama-7B q/k/v at 64 tokens, 192 units: 20.0 us with two-way splits, 15.1
+// us without).  Kernels with two resident blocks per compute unit (the
+// 256-thread FP8 variants) split a batch of one block per compute unit in two.
+template <typename T, typename X, typename TY, int NT, int U, int MAXN>
+void apply_launch_v(const PoolView& pv, const IoSet& ios, const int32_t* ids, int n,
+                    hipStream_t s) {
+  auto kern = k_bgmv_apply<T, X, TY, NT, U, MAXN>;
+  static const int nb = resident_blocks(reinterpret_cast<const void*>(kern), NT);
+  const long slots = (long)pv.n_cu * nb;
+  const int units = n * ios.n_io;
+  int nsplit = 1;
+  while ((long)units * nsplit * 2 <= slots && ios.max_d_out / (nsplit * 2) >= 512) nsplit *= 2;
+  const int rps = (((ios.max_d_out + nsplit - 1) / nsplit) + 63) & ~63;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(units, nsplit)), dim3(NT), 0, s, pv, ios, ids, n, nsplit,
+                     rps);
+}
+
 template <typename T, typename X, typename TY, int NT, int U>
-void apply_launch(const PoolView& pv, const IoSet& ios, const int32_t* ids, int n, dim3 grid,
-                  int nsplit, int rps, hipStream_t s) {
+void apply_launch(const PoolView& pv, const IoSet& ios, const int32_t* ids, int n,
+                  hipStream_t s) {
   // variant by the pool's longest B row, so short-row pools get lean kernels
   // (FP8 rows of 8 chunks at 512 threads take the loop body: an FP8 chunk
   // unpacks to twice the values of a 16-bit one)
   constexpr int kMaxN = (is_quant<T>() && NT == 512) ? 4 : 8;
   if (pv.max_nch <= 2)
-    hipLaunchKernelGGL((k_bgmv_apply<T, X, TY, NT, U, 2>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+    apply_launch_v<T, X, TY, NT, U, 2>(pv, ios, ids, n, s);
   else if (pv.max_nch <= 4 || kMaxN == 4)
-    hipLaunchKernelGGL((k_bgmv_apply<T, X, TY, NT, U, 4>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+    apply_launch_v<T, X, TY, NT, U, 4>(pv, ios, ids, n, s);
   else
-    hipLaunchKernelGGL((k_bgmv_apply<T, X, TY, NT, U, kMaxN>), grid, dim3(NT), 0, s, pv, ios, ids, n, nsplit, rps);
+    apply_launch_v<T, X, TY, NT, U, kMaxN>(pv, ios, ids, n, s);
 }
 
 template <typename T, typename X, typename TY>
@@ -425,25 +457,15 @@ hipError_t apply_t(const PoolView& pv, const IoSet& ios_in, const int32_t* ids, 
   std::stable_sort(ios.io, ios.io + ios.n_io, [](const IoDesc& a, const IoDesc& b) {
     return a.d_in + a.d_out > b.d_in + b.d_out;
   });
-  const int units = n * ios.n_io;
-  // Splitting a unit repeats its whole shrink, which costs more than it
-  // gains (measured, also when only the units with the largest B are split);
-  // split only while the split units still run in one round of one block per
-  // compute unit: a second, partly filled round costs more than the compute
-  // units one round leaves idle (Llama-7B q/k/v at 64 tokens, 192 units).
-  int nsplit = 1;
-  while ((long)units * nsplit * 2 <= pv.n_cu && ios.max_d_out / (nsplit * 2) >= 512) nsplit *= 2;
-  const int rps = (((ios.max_d_out + nsplit - 1) / nsplit) + 63) & ~63;
-  const dim3 grid(xcd_grid(units, nsplit));
   const int C = ios.max_d_in / E;
   if (C >= 512) {
     // FP8: one column chunk per thread (a wider row loops over the columns)
     if (is_quant<T>() || pick_u(ios.max_d_in, E, 512) == 1)
-      apply_launch<T, X, TY, 512, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
+      apply_launch<T, X, TY, 512, 1>(pv, ios, ids, n, s);
     else
-      apply_launch<T, X, TY, 512, is_quant<T>() ? 1 : 2>(pv, ios, ids, n, grid, nsplit, rps, s);
+      apply_launch<T, X, TY, 512, is_quant<T>() ? 1 : 2>(pv, ios, ids, n, s);
   } else {
-    apply_launch<T, X, TY, 256, 1>(pv, ios, ids, n, grid, nsplit, rps, s);
+    apply_launch<T, X, TY, 256, 1>(pv, ios, ids, n, s);
   }
   return hipGetLastError();
 }
