@@ -15,7 +15,8 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
+# LORA_MI355X_LIB: another build of the library (the profiling build)
+LIB_PATH = os.environ.get("LORA_MI355X_LIB") or os.path.join(_HERE, "liblora_mi355x.so")
 
 LORA_F32, LORA_F16, LORA_BF16, LORA_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
@@ -37,7 +38,8 @@ EXPORTS = (
     "lora_bgmv_apply", "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
     "lora_plan_get_stats", "lora_plan_export", "lora_plan_prepare", "lora_workspace_size",
     "lora_sgmv_shrink", "lora_sgmv_expand", "lora_apply", "lora_apply_noalloc", "lora_debug_resolve",
-    "lora_debug_gather", "lora_debug_decode", "lora_last_error", "lora_store_create",
+    "lora_debug_gather", "lora_debug_decode", "lora_debug_block_timeline", "lora_last_error",
+    "lora_store_create",
     "lora_store_destroy", "lora_store_add", "lora_store_ensure", "lora_store_get_stats",
 )
 
@@ -77,7 +79,7 @@ class PlanStats(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError("liblora_mi355x.so is not built: run `python gather_lora_matmul_amd/build.py`")
+        raise ImportError("%s is not built: run `python gather_lora_matmul_amd/build.py`" % LIB_PATH)
     # One HIP runtime per process: torch ships its own libamdhip64 (same soname
     # as ROCm's), and of two runtimes in one process only the first to start
     # sees the GPU.  With torch loaded first, this library binds to its runtime
@@ -98,6 +100,7 @@ def _load() -> ctypes.CDLL:
         "lora_pool_upload_scaled": [V, I32, I32, I32, F, V, V, V, V, V],
         "lora_pool_export_scales": [V, I32, I32, V, V],
         "lora_debug_decode": [I32, V, I64, V, V],
+        "lora_debug_block_timeline": [V, ctypes.c_size_t],
         "lora_store_create": [V, ctypes.POINTER(V)],
         "lora_store_destroy": [V],
         "lora_store_add": [V, I32, I32, I32, F, V, V, V, V],
@@ -587,6 +590,15 @@ def lora_debug_decode(dtype: int, src, dst, stream=None):
     _check_tensor(dst, "dst", LORA_F32, n)
     _check(_lib.lora_debug_decode(dtype, _dev_ptr(src), n, _dev_ptr(dst), _stream(stream)),
            "lora_debug_decode")
+
+
+def lora_debug_block_timeline(max_blocks: int) -> np.ndarray:
+    """Per-block records [max_blocks][8] (uint64) of the last fused decode
+    launch; raises LoraError(LORA_E_UNSUPPORTED) unless the library was built
+    with `build.py --timeline` (and loaded through LORA_MI355X_LIB)."""
+    out = np.zeros((max_blocks, 8), np.uint64)
+    _check(_lib.lora_debug_block_timeline(out.ctypes.data, out.nbytes), "lora_debug_block_timeline")
+    return out
 
 
 def lora_last_error() -> str:

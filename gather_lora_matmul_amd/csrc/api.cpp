@@ -272,4 +272,16 @@ lora_status lora_debug_decode(int32_t dtype, const void* src, int64_t n, float* 
   return hip_status(launch_debug_decode(dtype, src, n, dst, (hipStream_t)stream), "debug_decode");
 }
 
+lora_status lora_debug_block_timeline(void* host, size_t bytes) {
+  clear_error();
+  if (!host && bytes) return fail(LORA_E_ARG, "null host buffer");
+  if (bytes % (kTimelineWords * sizeof(uint64_t)))
+    return fail(LORA_E_ARG, "bytes must be a multiple of one %zu-byte record",
+                kTimelineWords * sizeof(uint64_t));
+  const hipError_t e = read_block_timeline(host, bytes);
+  if (e == hipErrorNotSupported)
+    return fail(LORA_E_UNSUPPORTED, "library built without LORA_BLOCK_TIMELINE");
+  return hip_status(e, "block timeline");
+}
+
 }  // extern "C"

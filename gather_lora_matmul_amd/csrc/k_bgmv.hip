@@ -235,17 +235,13 @@ __device__ __forceinline__ void bgmv_fused_fast(const PoolView& pv, const DevEnt
   valu_expand<T, TY, NT, NCH, 1>(pv, e, vsh, kMaxR, &s, yr, m_lo + NT * RU, m_hi);
 }
 
+// One (slice, token) unit, output rows [q * rps, (q + 1) * rps): the whole
+// shrink of the token into LDS, then the expand of those rows.  Returns at
+// once (block-uniform) for skipped tokens and empty row ranges.
 template <typename T, typename X, typename TY, int NT, int U, int MAXN>
-__global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
-                                                   const int32_t* __restrict__ ids, int n,
-                                                   int nsplit, int rps) {
-  __shared__ float part[(NT / 64) * kMaxR];
-  __shared__ float vsh[kMaxR];
-  int unit, q;
-  xcd_unit_split(blockIdx.x, nsplit, unit, q);
-  if (unit >= n * ios.n_io) return;
-  // slice-major: the launcher puts the costliest slices first, so their units
-  // are dispatched first and the cheaper ones fill the compute units that free up
+__device__ __forceinline__ void fused_unit(const PoolView& pv, const IoSet& ios,
+                                           const int32_t* __restrict__ ids, int n, int unit,
+                                           int q, int rps, float* part, float* vsh) {
   const int io_i = unit / n;
   const int i = unit - io_i * n;
   const IoDesc io = ios.io[io_i];
@@ -274,6 +270,52 @@ __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
   LORA_FUSED_CASE(16)
 #undef LORA_FUSED_CASE
   bgmv_fused_body<T, X, TY, NT, U, 0>(pv, e, io, i, m_lo, m_hi, part, vsh);
+}
+
+#ifdef LORA_BLOCK_TIMELINE
+// Profiling builds: per block of the last fused launch, {start, end} on the
+// 100 MHz constant clock, the hardware wave id register of wave 0, and the
+// block's unit: {slice, rank (0: skipped), token, row split}.
+__device__ unsigned long long block_timeline[kTimelineBlocks * kTimelineWords];
+#endif
+
+// Block = ((slice, token) unit, output-row split).
+template <typename T, typename X, typename TY, int NT, int U, int MAXN>
+__global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
+                                                   const int32_t* __restrict__ ids, int n,
+                                                   int nsplit, int rps) {
+  __shared__ float part[(NT / 64) * kMaxR];
+  __shared__ float vsh[kMaxR];
+#ifdef LORA_BLOCK_TIMELINE
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+#endif
+  int unit, q;
+  xcd_unit_split(blockIdx.x, nsplit, unit, q);
+  // slice-major: the launcher puts the costliest slices first, so their units
+  // are dispatched first and the cheaper ones fill the compute units that free up
+  if (unit < n * ios.n_io) fused_unit<T, X, TY, NT, U, MAXN>(pv, ios, ids, n, unit, q, rps, part, vsh);
+#ifdef LORA_BLOCK_TIMELINE
+  __syncthreads();
+  if (threadIdx.x == 0 && blockIdx.x < kTimelineBlocks) {
+    unsigned long long* r = block_timeline + (size_t)blockIdx.x * kTimelineWords;
+    int slice = -1, rank = 0, tok = -1;
+    if (unit < n * ios.n_io) {
+      const int io_i = unit / n;
+      tok = unit - io_i * n;
+      slice = ios.io[io_i].slice;
+      const int a = ids[tok];
+      if (adapter_in_table(pv, a)) rank = pv.entries[slice * pv.max_adapters + a].rank;
+    }
+    r[0] = t0;
+    r[1] = __builtin_amdgcn_s_memrealtime();
+    r[2] = __builtin_amdgcn_s_getreg((31 << 11) | 4);  // HW_ID: CU, SH, SE of this wave
+    r[3] = (unsigned long long)(unsigned)slice;
+    r[4] = rank;
+    r[5] = (unsigned long long)(unsigned)tok;
+    r[6] = q;
+    r[7] = 1;
+  }
+#endif
 }
 
 // Slices that share one x: block = (group of slices, token).  x of the token
@@ -522,6 +564,17 @@ hipError_t launch_bgmv_apply(const Types& ty, const PoolView& pv, const IoSet& i
       return yf ? apply_t<fp8_t, bf16_t, float>(pv, ios, ids, n, s)
                 : apply_t<fp8_t, bf16_t, bf16_t>(pv, ios, ids, n, s);
   }
+}
+
+hipError_t read_block_timeline(void* host, size_t bytes) {
+#ifdef LORA_BLOCK_TIMELINE
+  if (bytes > sizeof(block_timeline)) bytes = sizeof(block_timeline);
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(block_timeline), bytes, 0, hipMemcpyDeviceToHost);
+#else
+  (void)host;
+  (void)bytes;
+  return hipErrorNotSupported;
+#endif
 }
 
 }  // namespace lora

@@ -94,6 +94,12 @@ hipError_t launch_bgmv_expand(const Types& ty, const PoolView& pv, const IoDesc&
                               const float* tok_scale, hipStream_t s);
 hipError_t launch_bgmv_apply(const Types& ty, const PoolView& pv, const IoSet& ios,
                              const int32_t* ids, int32_t n, hipStream_t s);
+// Profiling builds (LORA_BLOCK_TIMELINE): per-block records of the last fused
+// decode launch, kTimelineWords 64-bit words per block for the first
+// kTimelineBlocks blocks; hipErrorNotSupported in other builds.
+constexpr int kTimelineBlocks = 65536;
+constexpr int kTimelineWords = 8;
+hipError_t read_block_timeline(void* host, size_t bytes);
 
 // Position in a launch's sequence of MFMA work for the persistent kernels:
 // the tiles of launch slice 0, then those of slice 1, ...; unit k of a tile is

@@ -361,6 +361,17 @@ lora_status lora_debug_gather(lora_pool* pool, int32_t slice, int32_t adapter, v
 lora_status lora_debug_decode(int32_t dtype, const void* src_dev, int64_t n, float* dst_dev,
                               void* stream);
 
+/* Profiling: per-block timeline of the last lora_bgmv_apply launch that ran
+ * one block per (slice, token) unit, in a library built with
+ * LORA_BLOCK_TIMELINE (build.py --timeline); LORA_E_UNSUPPORTED in other
+ * builds.  Copies up to `bytes` (a multiple of 64) into host memory: per block
+ * index, 8 uint64 words {start, end} (100 MHz constant clock), the hardware
+ * wave id register of the block's first wave (compute unit, shader array and
+ * engine fields), slice (-1: past the batch), rank (0: skipped token), token,
+ * row split, 1.  Records of blocks that did not run in that launch keep older
+ * contents.  Waits for the copy. */
+lora_status lora_debug_block_timeline(void* host, size_t bytes);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* lora_last_error(void);
 

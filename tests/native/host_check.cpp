@@ -29,6 +29,7 @@ hipError_t launch_bgmv_expand(const Types&, const PoolView&, const IoDesc&, cons
                               const int32_t*, int32_t, const float*, hipStream_t) STUB()
 hipError_t launch_bgmv_apply(const Types&, const PoolView&, const IoSet&, const int32_t*, int32_t,
                              hipStream_t) STUB()
+hipError_t read_block_timeline(void*, size_t) STUB()
 hipError_t launch_sgmv_shrink(const Types&, const PoolView&, const PlanView&, const IoDesc&, float*,
                               int32_t, hipStream_t) STUB()
 hipError_t launch_sgmv_expand(const Types&, const PoolView&, const PlanView&, const IoDesc&,
