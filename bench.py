@@ -86,6 +86,75 @@ def measured_traffic(workload: str, entry: str, src_hash: str):
     return rec.get("hbm_bytes_per_step")
 
 
+# rocprofv3 names of the kernels one step of each entry point runs
+STEP_KERNELS = {"lora_bgmv_apply": ("lora::k_bgmv_apply",),
+                "lora_apply": ("lora::k_apply_", "lora::k_sgmv_", "lora::k_short_"),
+                "lora_bgmv_shrink+expand": ("lora::k_bgmv_shrink", "lora::k_bgmv_expand"),
+                "lora_sgmv_shrink+expand": ("lora::k_sgmv_", "lora::k_apply_", "lora::k_short_")}
+COPY_BYTES = 64 << 20  # the --copy-calib copy
+
+
+def _counter_rows(run_dir: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    if not rows:
+        raise SystemExit("no %s records under %s" % (counter, run_dir))
+    return rows
+
+
+def record_traffic(fetch_dir: str, write_dir: str, workload: str, entry: str, src_hash: str,
+                   commands) -> dict:
+    """HBM bytes per step of `entry` from a FETCH_SIZE and a WRITE_SIZE
+    rocprofv3 run of `bench.py --copy-calib` (KiB per dispatch), each counter
+    scaled by what it reads for the 64 MiB copy of the same run; stored under
+    "workload/entry" in profiles/hbm_traffic.json with the kernels' source hash."""
+    per = {}
+    factors = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(run_dir, counter)
+        copies = sorted(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
+                        or "copy" in r["Kernel_Name"].lower() and "lora" not in r["Kernel_Name"])
+        big = copies[-10:]
+        if len(big) < 10 or big[0] < 0.25 * COPY_BYTES / 1024:
+            raise SystemExit("%s: the 64 MiB copies of --copy-calib are missing" % run_dir)
+        factors[counter] = COPY_BYTES / (float(np.median(big)) * 1024)
+        for r in rows:
+            name = r["Kernel_Name"]
+            if any(k in name for k in STEP_KERNELS[entry]):
+                per.setdefault(name, {}).setdefault(counter, []).append(float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit("no %s kernels in the counter records" % entry)
+    kernels, total = {}, 0.0
+    for name, c in sorted(per.items()):
+        f = float(np.mean(c.get("FETCH_SIZE", [0.0])))
+        w = float(np.mean(c.get("WRITE_SIZE", [0.0])))
+        b = (f * factors["FETCH_SIZE"] + w * factors["WRITE_SIZE"]) * 1024
+        kernels[name] = {"dispatches": len(c.get("FETCH_SIZE", [])), "fetch_KiB_mean": f,
+                         "write_KiB_mean": w, "hbm_bytes": b}
+        total += b
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            tj = json.load(fh)
+    except (OSError, ValueError):
+        tj = {}
+    tj["what"] = ("HBM bytes per step: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, two rocprofv3 "
+                  "--pmc runs of bench.py --copy-calib) each scaled by the counter's reading for a "
+                  "64 MiB device copy in the same run; mean over the step kernels' dispatches")
+    rec = {"hbm_bytes_per_step": total, "kernel_source_hash": src_hash,
+           "fetch_factor": factors["FETCH_SIZE"], "write_factor": factors["WRITE_SIZE"],
+           "kernels": kernels, "commands": list(commands)}
+    tj.setdefault("records", {})["%s/%s" % (workload, entry)] = rec
+    with open(path, "w") as fh:
+        json.dump(tj, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return rec
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -151,6 +220,8 @@ class Runner:
         self.planned = planned or cfg in (3, 4)
         self.mode = mode
         self.qkv = qkv
+        # traffic records exist only for the workloads' own batches
+        self.traffic_ok = qkv is None and n_tokens is None
         self.slices = slices = [0, 1, 2] if qkv else list(range(len(wl.slices)))
         n_batches = n_batches or (4 if self.planned else 16)
         t0 = time.perf_counter()
@@ -259,7 +330,8 @@ class Runner:
                             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                             "basis": "algorithmic bytes / (HIP-event time of the timed steps / "
                                      "steps), launch gaps included",
-                            "traffic": measured_traffic(self.wl.name, self.entry, self.src_hash)},
+                            "traffic": (measured_traffic(self.wl.name, self.entry, self.src_hash)
+                                        if self.traffic_ok else None)},
                "kernel_source_hash": self.src_hash, "pool_setup_s": self.setup_s}
         if self.plan_host:
             rec["plan_host_us"] = self.plan_host
@@ -396,7 +468,24 @@ def main():
                     help="time only the headline workload")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 64 MiB device copy 10x (HBM counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no timing: store the HBM bytes per step of --workload (and --planned) "
+                         "from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run into "
+                         "profiles/hbm_traffic.json")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --record-traffic: the profiling commands, kept in the record")
     args = ap.parse_args()
+    if args.record_traffic:
+        cfg = WORKLOADS[args.workload]
+        planned = args.planned or cfg in (3, 4)
+        entry = (("lora_apply" if planned else "lora_bgmv_apply") if args.mode == "fused"
+                 else ("lora_sgmv_shrink+expand" if planned else "lora_bgmv_shrink+expand"))
+        rec = record_traffic(args.record_traffic[0], args.record_traffic[1], args.workload, entry,
+                             source_hash(PLANNED_SOURCES if planned else BGMV_SOURCES), args.command)
+        print(json.dumps({"workload": args.workload, "entry": entry,
+                          "hbm_MB_per_step": rec["hbm_bytes_per_step"] / 1e6,
+                          "fetch_factor": rec["fetch_factor"], "write_factor": rec["write_factor"]}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this LoRA-apply path runs on a single GPU; --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
