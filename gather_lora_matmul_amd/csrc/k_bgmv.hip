@@ -279,20 +279,105 @@ __device__ __forceinline__ void fused_unit(const PoolView& pv, const IoSet& ios,
 __device__ unsigned long long block_timeline[kTimelineBlocks * kTimelineWords];
 #endif
 
+// ---- longest units first ---------------------------------------------------------
+// When the adapters differ in rank, (slice, token) units differ in cost by up
+// to 16x, and the order in which blocks are dispatched sets the step time: a
+// costly unit dispatched late ends the launch.  With `lpt` set (one unit per
+// block, at most kLptMax units), block b runs the unit at position b of the
+// batch ordered by decreasing weight bytes r * (d_in + d_out), ties by unit
+// index.  Every block ranks the units itself in LDS (the ranks from the
+// adapter table, units^2 / NT comparisons): no pre-pass launch, no scratch.
+constexpr int kLptMax = 1024;
+constexpr int kLptUnitBits = 10;
+constexpr unsigned kLptCostMax = (1u << (32 - kLptUnitBits)) - 1;
+
+// Unit at position p of the cost order; all threads call it, the result is
+// uniform.  key: kLptMax words, cnt: NT + 1 words, es/ew: LORA_MAX_IO words.
+template <int NT>
+__device__ __forceinline__ int unit_by_cost(const PoolView& pv, const IoSet& ios,
+                                            const int32_t* __restrict__ ids, int n, int p,
+                                            unsigned* key, int* cnt, int* es, int* ew) {
+  const int units = n * ios.n_io;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    for (int j = 0; j < ios.n_io; ++j) {  // uniform index into the argument block
+      es[j] = ios.io[j].slice;
+      ew[j] = (ios.io[j].d_in + ios.io[j].d_out + 1023) >> 10;
+    }
+  }
+  __syncthreads();
+  const int u4 = (units + 3) & ~3;
+  for (int u = t; u < u4; u += NT) {
+    unsigned k = 0xFFFFFFFFu;  // padding ranks after every unit
+    if (u < units) {
+      const int j = u / n;
+      const int a = ids[u - j * n];
+      unsigned c = 0;
+      if (adapter_in_table(pv, a))
+        c = (unsigned)pv.entries[es[j] * pv.max_adapters + a].rank * (unsigned)ew[j];
+      k = ((kLptCostMax - min(c, kLptCostMax)) << kLptUnitBits) | (unsigned)u;
+    }
+    key[u] = k;
+  }
+  __syncthreads();
+  // R threads per candidate unit, each counting the keys below its key in one
+  // part of the list
+  const int upad = (units + 63) & ~63;
+  const int R = upad <= NT ? NT / upad : 1;
+  const int g = t / upad;
+  const int per = ((u4 / 4 + R - 1) / R) * 4;
+  int found = -1;
+  for (int u = t - g * upad; u < units && g < R; u += NT) {
+    const unsigned ku = key[u];
+    const int k_end = min(u4, (g + 1) * per);
+    int below = 0;
+    for (int k = g * per; k < k_end; k += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(key + k);
+      below += (v.x < ku) + (v.y < ku) + (v.z < ku) + (v.w < ku);
+    }
+    if (R == 1) {
+      if (below == p) found = u;
+    } else {
+      cnt[t] = below;
+    }
+  }
+  if (R > 1) {
+    __syncthreads();
+    if (t < units && t < upad) {
+      int below = 0;
+      for (int gg = 0; gg < R; ++gg) below += cnt[gg * upad + t];
+      if (below == p) found = t;
+    }
+  }
+  if (found >= 0) cnt[NT] = found;  // keys are distinct: one writer
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(cnt[NT]);
+}
+
 // Block = ((slice, token) unit, output-row split).
 template <typename T, typename X, typename TY, int NT, int U, int MAXN>
 __global__ __launch_bounds__(NT) void k_bgmv_apply(PoolView pv, IoSet ios,
                                                    const int32_t* __restrict__ ids, int n,
-                                                   int nsplit, int rps) {
+                                                   int nsplit, int rps, int lpt) {
   __shared__ float part[(NT / 64) * kMaxR];
   __shared__ float vsh[kMaxR];
+  __shared__ __align__(16) unsigned key[kLptMax];
+  __shared__ int cnt[NT + 1];
+  __shared__ int es[LORA_MAX_IO], ew[LORA_MAX_IO];
 #ifdef LORA_BLOCK_TIMELINE
   const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
 #endif
   int unit, q;
-  xcd_unit_split(blockIdx.x, nsplit, unit, q);
-  // slice-major: the launcher puts the costliest slices first, so their units
-  // are dispatched first and the cheaper ones fill the compute units that free up
+  if (lpt) {
+    q = 0;
+    unit = blockIdx.x < n * ios.n_io
+               ? unit_by_cost<NT>(pv, ios, ids, n, blockIdx.x, key, cnt, es, ew)
+               : n * ios.n_io;
+  } else {
+    // slice-major: the launcher puts the costliest slices first, so their units
+    // are dispatched first and the cheaper ones fill the compute units that free up
+    xcd_unit_split(blockIdx.x, nsplit, unit, q);
+  }
   if (unit < n * ios.n_io) fused_unit<T, X, TY, NT, U, MAXN>(pv, ios, ids, n, unit, q, rps, part, vsh);
 #ifdef LORA_BLOCK_TIMELINE
   __syncthreads();
@@ -458,8 +543,10 @@ void apply_launch_v(const PoolView& pv, const IoSet& ios, const int32_t* ids, in
   int nsplit = 1;
   while ((long)units * nsplit * 2 <= slots && ios.max_d_out / (nsplit * 2) >= 512) nsplit *= 2;
   const int rps = (((ios.max_d_out + nsplit - 1) / nsplit) + 63) & ~63;
+  // longest units first when ranks differ and the units take more than one round
+  const int lpt = pv.mixed_ranks && nsplit == 1 && units > slots && units <= kLptMax ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3(xcd_grid(units, nsplit)), dim3(NT), 0, s, pv, ios, ids, n, nsplit,
-                     rps);
+                     rps, lpt);
 }
 
 template <typename T, typename X, typename TY, int NT, int U>

@@ -36,6 +36,7 @@ struct PoolView {
   int32_t max_adapters;
   int32_t max_nch;            // 16-byte chunks in the longest stored B row of the pool
   int32_t n_cu;               // compute units of the pool's device
+  int32_t mixed_ranks;        // 1: the resident adapters of this table differ in rank
 };
 
 // Per-slice input/output of one launch.

@@ -128,12 +128,15 @@ lora_status publish_table(lora_pool* p, hipStream_t upload, hipStream_t compute)
   std::vector<DevEntry> ent(p->slots.size());
   std::vector<int32_t> ids;
   ids.reserve((size_t)p->n_pages);
+  int r_min = 0, r_max = 0;
   for (int s = 0; s < p->n_slices; ++s)
     for (int a = 0; a < p->max_adapters; ++a) {
       const Slot& sl = p->slot(s, a);
       DevEntry& e = ent[(size_t)s * p->max_adapters + a];
       memset(&e, 0, sizeof(e));
       if (!sl.rank) continue;
+      r_min = r_min ? std::min(r_min, sl.rank) : sl.rank;
+      r_max = std::max(r_max, sl.rank);
       e.rank = sl.rank;
       e.rs = sl.rs;
       e.scale = sl.scale;
@@ -158,6 +161,7 @@ lora_status publish_table(lora_pool* p, hipStream_t upload, hipStream_t compute)
   if (ids.size() > p->page_ids_cap)
     return fail(LORA_E_STATE, "page table of %zu words exceeds its %zu", ids.size(), p->page_ids_cap);
   DevTable& t = p->tables[1 - p->cur];
+  t.mixed_ranks = r_min != r_max;
   const size_t eb = sizeof(DevEntry) * ent.size();
   const size_t ib = sizeof(int32_t) * ids.size();
   const size_t ioff = (eb + 255) & ~(size_t)255;

@@ -19,6 +19,7 @@ struct DevTable {
   bool staged_pending = false;
   hipEvent_t retired = nullptr;   // launches that read this table have completed
   bool retired_pending = false;
+  bool mixed_ranks = false;       // the resident adapters have more than one rank
 };
 
 struct Quarantine {
@@ -119,6 +120,7 @@ struct lora_pool {
     v.max_adapters = max_adapters;
     v.max_nch = rs_of(max_rank) * elt / 16;
     v.n_cu = n_cu;
+    v.mixed_ranks = tables[cur].mixed_ranks ? 1 : 0;
     return v;
   }
   lora::IoDesc io(int slice, const void* x, void* y) const {
