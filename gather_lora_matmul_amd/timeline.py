@@ -55,17 +55,28 @@ def summarize(rec: np.ndarray, title: str) -> str:
     cus = collections.defaultdict(list)
     for i, k in enumerate(key):
         cus[k].append(i)
-    gaps, idle_end = [], []
+    # per compute unit: the union of its blocks' intervals (blocks may overlap
+    # when several are resident at once), the idle gaps between busy stretches
+    gaps, idle_end, busy_t, conc = [], [], 0.0, 1
     for v in cus.values():
         v = sorted(v, key=lambda j: t0[j])
-        gaps += [t0[b] - t1[a] for a, b in zip(v, v[1:])]
-        idle_end.append(t1.max() - t1[v[-1]])
+        cur_s, cur_e = t0[v[0]], t1[v[0]]
+        for j in v[1:]:
+            conc = max(conc, int(((t0[v] <= t0[j]) & (t1[v] > t0[j])).sum()))
+            if t0[j] > cur_e:
+                gaps.append(t0[j] - cur_e)
+                busy_t += cur_e - cur_s
+                cur_s, cur_e = t0[j], t1[j]
+            else:
+                cur_e = max(cur_e, t1[j])
+        busy_t += cur_e - cur_s
+        idle_end.append(t1.max() - cur_e)
     gaps = np.array(gaps) if gaps else np.zeros(1)
     per_cu = collections.Counter(len(v) for v in cus.values())
-    busy = d.sum() / (len(cus) * t1.max())
-    out += ["compute units %d (blocks per unit: %s); busy fraction %.2f" % (
-                len(cus), ", ".join("%d: %d" % kv for kv in sorted(per_cu.items())), busy),
-            "gap between consecutive blocks on one unit: median %.2f us, p90 %.2f, max %.2f; "
+    busy = busy_t / (len(cus) * t1.max())
+    out += ["compute units %d (blocks per unit: %s; at most %d at once); busy fraction %.2f" % (
+                len(cus), ", ".join("%d: %d" % kv for kv in sorted(per_cu.items())), conc, busy),
+            "idle gaps between busy stretches of one unit: median %.2f us, p90 %.2f, max %.2f; "
             "idle after its last block: median %.1f us" % (
                 np.median(gaps), np.percentile(gaps, 90), gaps.max(), np.median(idle_end)), ""]
     return "\n".join(out)
