@@ -463,6 +463,9 @@ def main():
     ap.add_argument("--l-long", type=int, default=0,
                     help="planned batches: groups shorter than this run as short VALU items "
                          "(0: every group of a 16-bit pool is an MFMA tile)")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="decode workloads: tokens per batch instead of the workload's own "
+                         "(a profiling line, not the headline)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time only the headline workload")
@@ -493,7 +496,8 @@ def main():
 
     import torch
     torch.cuda.set_device(0)
-    head = Runner(args.workload, args.mode, args.planned, args.batches, args.l_long)
+    head = Runner(args.workload, args.mode, args.planned, args.batches, args.l_long,
+                  n_tokens=args.tokens)
     rec = head.record(args.steps, args.warmup)
     wl = head.wl
     cfg = WORKLOADS[args.workload]
