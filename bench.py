@@ -71,12 +71,12 @@ def source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, entry: str, src_hash: str):
+def measured_traffic(workload: str, entry: str, src_hash: str, path: str = None):
     """HBM bytes per step of `entry` on `workload` from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (profiles/hbm_traffic.json), or None if
     there is none or the kernels' sources changed since it was taken."""
     try:
-        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+        with open(path or os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
             tj = json.load(f)
     except (OSError, ValueError):
         return None
@@ -107,7 +107,7 @@ def _counter_rows(run_dir: str, counter: str):
 
 
 def record_traffic(fetch_dir: str, write_dir: str, workload: str, entry: str, src_hash: str,
-                   commands) -> dict:
+                   commands, path: str = None) -> dict:
     """HBM bytes per step of `entry` from a FETCH_SIZE and a WRITE_SIZE
     rocprofv3 run of `bench.py --copy-calib` (KiB per dispatch), each counter
     scaled by what it reads for the 64 MiB copy of the same run; stored under
@@ -136,7 +136,7 @@ def record_traffic(fetch_dir: str, write_dir: str, workload: str, entry: str, sr
         kernels[name] = {"dispatches": len(c.get("FETCH_SIZE", [])), "fetch_KiB_mean": f,
                          "write_KiB_mean": w, "hbm_bytes": b}
         total += b
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as fh:
             tj = json.load(fh)
