@@ -248,6 +248,42 @@ lora_status lora_store_ensure(lora_store* s, int32_t n, const int32_t* adapters,
     LORA_HIP(hipEventSynchronize(s->done));
     s->done_pending = false;
   }
+  // host and device staging for this call, sized before any pool state
+  // changes (a failed allocation leaves the pool as it was): page ids of every
+  // load (free pages first, then evicted ones) and of the evicted pages no load
+  // takes, and the page images of every load
+  int64_t gain_pages = 0;
+  for (int a : victims)
+    for (int sl = 0; sl < p->n_slices; ++sl) gain_pages += (int64_t)p->slot(sl, a).pages.size();
+  const int64_t from_evicted = std::max<int64_t>(0, need - (int64_t)p->free_list.size());
+  const int64_t n_ids = need + (gain_pages - from_evicted);
+  if ((size_t)n_ids > s->h_ids_cap) {
+    if (s->h_ids) (void)hipHostFree(s->h_ids);
+    s->h_ids = nullptr;
+    s->h_ids_cap = 0;
+    const size_t cap = (size_t)n_ids + (size_t)n_ids / 2 + 1024;
+    const hipError_t e = hipHostMalloc((void**)&s->h_ids, cap * sizeof(int32_t), hipHostMallocDefault);
+    if (e != hipSuccess) {
+      s->h_ids = nullptr;
+      return fail(LORA_E_NOMEM, "pinned staging of %zu page ids: %s", cap, hipGetErrorString(e));
+    }
+    s->h_ids_cap = cap;
+  }
+  const size_t img_bytes = (size_t)(need * p->page_bytes);
+  const size_t ids_off = (img_bytes + 255) & ~size_t(255);
+  const size_t stage_bytes = ids_off + sizeof(int32_t) * (size_t)std::max<int64_t>(n_ids, 1);
+  if (stage_bytes > s->d_cap) {
+    if (s->d_stage) (void)hipFree(s->d_stage);  // the last ensure's use of it has completed
+    s->d_stage = nullptr;
+    s->d_cap = 0;
+    const size_t cap = stage_bytes + stage_bytes / 4 + (1 << 20);
+    const hipError_t e = hipMalloc((void**)&s->d_stage, cap);
+    if (e != hipSuccess) {
+      s->d_stage = nullptr;
+      return fail(LORA_E_NOMEM, "device staging of %zu bytes: %s", cap, hipGetErrorString(e));
+    }
+    s->d_cap = cap;
+  }
   // evict (host state): their pages become this call's second pool of pages
   std::vector<int32_t> evicted;
   for (int a : victims)
@@ -279,31 +315,15 @@ lora_status lora_store_ensure(lora_store* s, int32_t n, const int32_t* adapters,
   // (loads into free pages come first: pages are assigned in that order)
   std::vector<int32_t> leftover(evicted.begin() + (ptrdiff_t)ev_next, evicted.end());
   // ids: [free loads' pages | evicted loads' pages | leftover evicted pages]
-  const int64_t n_ids = stage_pages + (int64_t)leftover.size();
-  if ((size_t)n_ids > s->h_ids_cap) {
-    if (s->h_ids) (void)hipHostFree(s->h_ids);
-    s->h_ids = nullptr;
-    const size_t cap = (size_t)n_ids + (size_t)n_ids / 2 + 1024;
-    LORA_HIP(hipHostMalloc((void**)&s->h_ids, cap * sizeof(int32_t), hipHostMallocDefault));
-    s->h_ids_cap = cap;
-  }
   int64_t k = 0, n_free_pages = 0;
   for (const Load& ld : loads) {
     for (int32_t pg : ld.pages) s->h_ids[k++] = pg;
     if (!ld.into_evicted) n_free_pages += (int64_t)ld.pages.size();
   }
   for (int32_t pg : leftover) s->h_ids[k++] = pg;
-  const size_t img_bytes = (size_t)(stage_pages * p->page_bytes);
-  const size_t ids_off = (img_bytes + 255) & ~size_t(255);
-  const size_t stage_bytes = ids_off + sizeof(int32_t) * (size_t)std::max<int64_t>(n_ids, 1);
-  if (stage_bytes > s->d_cap) {
-    if (s->d_stage) (void)hipFree(s->d_stage);  // the last ensure's use of it has completed
-    s->d_stage = nullptr;
-    s->d_cap = 0;
-    const size_t cap = stage_bytes + stage_bytes / 4 + (1 << 20);
-    LORA_HIP(hipMalloc((void**)&s->d_stage, cap));
-    s->d_cap = cap;
-  }
+  if (k != n_ids || stage_pages != need)
+    return fail(LORA_E_STATE, "internal: %lld page ids staged, %lld expected", (long long)k,
+                (long long)n_ids);
   const int32_t* d_ids = (const int32_t*)(s->d_stage + ids_off);
   if (n_ids > 0)
     LORA_HIP(hipMemcpyAsync(s->d_stage + ids_off, s->h_ids, sizeof(int32_t) * (size_t)n_ids,

@@ -205,9 +205,13 @@ lora_status lora_store_add(lora_store* store, int32_t adapter, int32_t slice, in
  * after this call see the new residency, launches enqueued before it keep the
  * table they were given.  Launches on other streams must be ordered by the
  * caller.  Plans built before a call that changed residency are refused
- * (rebuild them).  Host waits: only for the previous call's copies.  Errors:
- * LORA_E_NOT_RESIDENT (an adapter not in the store), LORA_E_NOMEM (the list
- * does not fit the pool), with the pool unchanged. */
+ * (rebuild them).  Host waits: for the previous call's copies, and, when a
+ * request needs more staging than any before it, for the reallocation of the
+ * store's device staging buffer.  Errors: LORA_E_NOT_RESIDENT (an adapter not
+ * in the store), LORA_E_NOMEM (the list does not fit the pool, or staging
+ * memory cannot be allocated), with the pool unchanged; LORA_E_HIP from a
+ * runtime call after the loads were enqueued leaves the pool unusable
+ * (destroy it). */
 lora_status lora_store_ensure(lora_store* store, int32_t n, const int32_t* adapters_host,
                               void* upload_stream, void* compute_stream);
 lora_status lora_store_get_stats(const lora_store* store, lora_store_stats* out);
