@@ -43,6 +43,20 @@ CSRC = os.path.join(ROOT, "gather_lora_matmul_amd", "csrc")
 BGMV_SOURCES = ("k_bgmv.hip", "kcommon.h", "kvalu.h", "lora_internal.h")
 PLANNED_SOURCES = ("k_sgmv.hip", "kmfma.h", "kcommon.h", "kvalu.h", "lora_internal.h",
                    "layout.cpp", "plan.cpp")
+DEVPLAN_SOURCES = ("k_devplan.hip", "devplan.h", "k_sgmv.hip", "kmfma.h", "kcommon.h", "kvalu.h",
+                   "lora_internal.h")
+
+
+def entry_of(planned: bool, devplan: bool, mode: str) -> str:
+    if devplan:
+        return "lora_bgmv_apply_planned"
+    if mode == "fused":
+        return "lora_apply" if planned else "lora_bgmv_apply"
+    return "lora_sgmv_shrink+expand" if planned else "lora_bgmv_shrink+expand"
+
+
+def sources_of(planned: bool, devplan: bool):
+    return DEVPLAN_SOURCES if devplan else (PLANNED_SOURCES if planned else BGMV_SOURCES)
 
 
 def algorithmic_bytes(wl, ids: np.ndarray, slices, elt_y: int, shared_x: bool = False) -> int:
@@ -206,9 +220,11 @@ class Runner:
     workspaces, and the step that applies one batch."""
 
     def __init__(self, name: str, mode: str = "fused", planned: bool = False, n_batches=None,
-                 l_long: int = 0, qkv=None, n_tokens=None):
+                 l_long: int = 0, qkv=None, n_tokens=None, devplan: bool = False):
         """qkv: None, or "separate" / "shared": q, k and v (slices 0-2) reading
-        one x buffer, without or with an x_group (decode BGMV only)."""
+        one x buffer, without or with an x_group (decode BGMV only).  devplan:
+        decode workloads through lora_bgmv_apply_planned (tokens grouped by
+        adapter on the device)."""
         import torch
 
         import gather_lora_matmul_amd as L
@@ -218,6 +234,9 @@ class Runner:
         cfg = WORKLOADS[name]
         self.wl = wl = W.make_workload(cfg)
         self.planned = planned or cfg in (3, 4)
+        self.devplan = devplan and not self.planned
+        if self.devplan:
+            mode = "fused"
         self.mode = mode
         self.qkv = qkv
         # traffic records exist only for the workloads' own batches
@@ -263,16 +282,25 @@ class Runner:
         self.stream_h = self.stream.cuda_stream
         # fused steps: arguments checked and marshalled once per rotating batch
         self.calls = []
+        self.ws_dev = None
+        if self.devplan:
+            n_max = max(len(b.ids) for b in self.batches)
+            self.ws_dev = torch.empty(L.lora_bgmv_planned_workspace_size(self.sp.handle, slices, n_max),
+                                      dtype=torch.uint8, device="cuda")
         if mode == "fused":
             for k, b in enumerate(self.batches):
                 group = 1 if qkv == "shared" else 0
                 io = [(s, self.xs[k][j], self.ys[k][j], group) for j, s in enumerate(slices)]
-                self.calls.append(
-                    L.prepare_apply(self.sp.handle, self.plans[k], io, self.ydt, workspace=self.wss[k])
-                    if self.planned else L.prepare_bgmv_apply(self.sp.handle, io, self.ids_d[k], self.ydt))
-        self.entry = (("lora_apply" if self.planned else "lora_bgmv_apply") if mode == "fused"
-                      else ("lora_sgmv_shrink+expand" if self.planned else "lora_bgmv_shrink+expand"))
-        self.src_hash = source_hash(PLANNED_SOURCES if self.planned else BGMV_SOURCES)
+                if self.planned:
+                    c = L.prepare_apply(self.sp.handle, self.plans[k], io, self.ydt, workspace=self.wss[k])
+                elif self.devplan:
+                    c = L.prepare_bgmv_apply_planned(self.sp.handle, io, self.ids_d[k], self.ydt,
+                                                     self.ws_dev)
+                else:
+                    c = L.prepare_bgmv_apply(self.sp.handle, io, self.ids_d[k], self.ydt)
+                self.calls.append(c)
+        self.entry = entry_of(self.planned, self.devplan, mode)
+        self.src_hash = source_hash(sources_of(self.planned, self.devplan))
 
     def step(self, i: int):
         L, k = self.L, i % len(self.batches)
@@ -460,6 +488,9 @@ def main():
     ap.add_argument("--planned", action="store_true",
                     help="decode workloads: plan each batch on the host and run lora_apply "
                          "(the SGMV path) instead of lora_bgmv_apply")
+    ap.add_argument("--devplan", action="store_true",
+                    help="decode workloads: group the tokens by adapter on the device "
+                         "(lora_bgmv_apply_planned) instead of lora_bgmv_apply")
     ap.add_argument("--l-long", type=int, default=0,
                     help="planned batches: groups shorter than this run as short VALU items "
                          "(0: every group of a 16-bit pool is an MFMA tile)")
@@ -481,10 +512,10 @@ def main():
     if args.record_traffic:
         cfg = WORKLOADS[args.workload]
         planned = args.planned or cfg in (3, 4)
-        entry = (("lora_apply" if planned else "lora_bgmv_apply") if args.mode == "fused"
-                 else ("lora_sgmv_shrink+expand" if planned else "lora_bgmv_shrink+expand"))
+        devplan = args.devplan and not planned
+        entry = entry_of(planned, devplan, args.mode)
         rec = record_traffic(args.record_traffic[0], args.record_traffic[1], args.workload, entry,
-                             source_hash(PLANNED_SOURCES if planned else BGMV_SOURCES), args.command)
+                             source_hash(sources_of(planned, devplan)), args.command)
         print(json.dumps({"workload": args.workload, "entry": entry,
                           "hbm_MB_per_step": rec["hbm_bytes_per_step"] / 1e6,
                           "fetch_factor": rec["fetch_factor"], "write_factor": rec["write_factor"]}))
@@ -497,7 +528,7 @@ def main():
     import torch
     torch.cuda.set_device(0)
     head = Runner(args.workload, args.mode, args.planned, args.batches, args.l_long,
-                  n_tokens=args.tokens)
+                  n_tokens=args.tokens, devplan=args.devplan)
     rec = head.record(args.steps, args.warmup)
     wl = head.wl
     cfg = WORKLOADS[args.workload]
@@ -541,21 +572,25 @@ def main():
         extra = {}
         steps = min(args.steps, 50)
         warm = min(args.warmup, 5)
-        for name, planned, qkv, ntok in (("llama7b_decode_bgmv", False, "separate", None),
-                                         ("llama7b_decode_bgmv", False, "shared", None),
-                                         ("llama7b_decode_bgmv", False, "separate", 256),
-                                         ("llama7b_decode_bgmv", False, "shared", 256),
-                                         ("llama7b_decode_bgmv_fp8", False, None, None),
-                                         ("hetero_decode_bgmv", False, None, None),
-                                         ("hetero_decode_bgmv", True, None, None),
-                                         ("llama13b_prefill_sgmv", True, None, None),
-                                         ("llama70b_mixed_apply", True, None, None)):
+        for name, planned, qkv, ntok, dp in (("llama7b_decode_bgmv", False, "separate", None, False),
+                                             ("llama7b_decode_bgmv", False, "shared", None, False),
+                                             ("llama7b_decode_bgmv", False, "separate", 256, False),
+                                             ("llama7b_decode_bgmv", False, "shared", 256, False),
+                                             ("llama7b_decode_bgmv", False, None, None, True),
+                                             ("llama7b_decode_bgmv_fp8", False, None, None, False),
+                                             ("hetero_decode_bgmv", False, None, None, False),
+                                             ("hetero_decode_bgmv", False, None, None, True),
+                                             ("hetero_decode_bgmv", True, None, None, False),
+                                             ("llama13b_prefill_sgmv", True, None, None, False),
+                                             ("llama70b_mixed_apply", True, None, None, False)):
             key = name + ("/planned" if planned and WORKLOADS[name] in (1, 2) else "")
+            key += "/device_planned" if dp else ""
             key += "/qkv_%s_x" % qkv if qkv else ""
             key += "_%dtok" % ntok if ntok else ""
-            if name == args.workload and planned == head.planned and not qkv:
+            if (name == args.workload and planned == head.planned and dp == head.devplan
+                    and not qkv):
                 continue
-            r = Runner(name, "fused", planned, qkv=qkv, n_tokens=ntok)
+            r = Runner(name, "fused", planned, qkv=qkv, n_tokens=ntok, devplan=dp)
             extra[key] = r.record(steps, warm)
             r.close()
             print("[bench] %s: %.1f us per step, %.3f of 8 TB/s" % (

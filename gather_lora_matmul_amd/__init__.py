@@ -35,7 +35,8 @@ EXPORTS = (
     "lora_pool_free_pages", "lora_pool_upload", "lora_pool_upload_scaled", "lora_pool_evict",
     "lora_page_table_build", "lora_pool_export_entry", "lora_pool_export_scales",
     "lora_pool_read_pages", "lora_bgmv_shrink", "lora_bgmv_expand",
-    "lora_bgmv_apply", "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
+    "lora_bgmv_apply", "lora_bgmv_planned_workspace_size", "lora_bgmv_apply_planned",
+    "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
     "lora_plan_get_stats", "lora_plan_export", "lora_plan_prepare", "lora_workspace_size",
     "lora_sgmv_shrink", "lora_sgmv_expand", "lora_apply", "lora_apply_noalloc", "lora_debug_resolve",
     "lora_debug_gather", "lora_debug_decode", "lora_debug_block_timeline", "lora_last_error",
@@ -113,6 +114,9 @@ def _load() -> ctypes.CDLL:
         "lora_bgmv_shrink": [V, I32, V, V, I32, V, I32, V],
         "lora_bgmv_expand": [V, I32, V, I32, V, I32, V, V, I32, V],
         "lora_bgmv_apply": [V, I32, ctypes.POINTER(Io), V, I32, I32, V],
+        "lora_bgmv_planned_workspace_size": [V, I32, ctypes.POINTER(Io), I32,
+                                             ctypes.POINTER(ctypes.c_size_t)],
+        "lora_bgmv_apply_planned": [V, I32, ctypes.POINTER(Io), V, I32, I32, V, ctypes.c_size_t, V],
         "lora_plan_create": [V, I32, ctypes.POINTER(V)],
         "lora_plan_destroy": [V],
         "lora_plan_build": [V, V, I32, I32, V],
@@ -415,6 +419,28 @@ def lora_bgmv_apply(pool: int, ios: Sequence[Tuple[int, object, object]], ids, y
                                 _stream(stream)), "lora_bgmv_apply")
 
 
+def lora_bgmv_planned_workspace_size(pool: int, slices: Sequence[int], n: int) -> int:
+    """Workspace bytes of lora_bgmv_apply_planned for n tokens over `slices`."""
+    arr = _slice_ios(slices)
+    out = ctypes.c_size_t()
+    _check(_lib.lora_bgmv_planned_workspace_size(pool, len(slices), arr, int(n), ctypes.byref(out)),
+           "lora_bgmv_planned_workspace_size")
+    return int(out.value)
+
+
+def lora_bgmv_apply_planned(pool: int, ios: Sequence[Tuple[int, object, object]], ids, y_dtype: int,
+                            workspace, stream=None):
+    """lora_bgmv_apply with the tokens grouped by adapter on the device (ids on
+    the device); workspace: a device tensor of lora_bgmv_planned_workspace_size
+    bytes, 256-byte aligned (torch's allocations are)."""
+    _check_ids(ids)
+    _check_io(pool, ios, int(ids.shape[0]), y_dtype)
+    arr = _ios(ios)
+    wp, wb = _ws(workspace)
+    _check(_lib.lora_bgmv_apply_planned(pool, len(ios), arr, _dev_ptr(ids), int(ids.shape[0]), y_dtype,
+                                        wp, wb, _stream(stream)), "lora_bgmv_apply_planned")
+
+
 # ----------------------------------------------------------------------------
 # SGMV
 # ----------------------------------------------------------------------------
@@ -560,6 +586,17 @@ def prepare_bgmv_apply(pool: int, ios: Sequence[Tuple[int, object, object]], ids
     return PreparedCall(_lib.lora_bgmv_apply, (pool, len(ios), arr, _dev_ptr(ids),
                                                int(ids.shape[0]), y_dtype),
                         "lora_bgmv_apply", (ios, ids, arr))
+
+
+def prepare_bgmv_apply_planned(pool: int, ios: Sequence[Tuple[int, object, object]], ids,
+                               y_dtype: int, workspace) -> PreparedCall:
+    _check_ids(ids)
+    _check_io(pool, ios, int(ids.shape[0]), y_dtype)
+    arr = _ios(ios)
+    wp, wb = _ws(workspace)
+    return PreparedCall(_lib.lora_bgmv_apply_planned, (pool, len(ios), arr, _dev_ptr(ids),
+                                                       int(ids.shape[0]), y_dtype, wp, wb),
+                        "lora_bgmv_apply_planned", (ios, ids, arr, workspace))
 
 
 def prepare_apply(pool: int, plan: int, ios: Sequence[Tuple[int, object, object]], y_dtype: int,

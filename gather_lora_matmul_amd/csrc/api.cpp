@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstring>
 
+#include "devplan.h"
 #include "runtime.h"
 
 using namespace lora;
@@ -123,6 +124,37 @@ lora_status find_layout(const lora_plan* pl, const IoSet& ios, const void* ws, s
   return LORA_OK;
 }
 
+// Launch shape and workspace layout of a device-planned decode call; refuses
+// what the MFMA tiles cannot take.
+lora_status devplan_shape(const lora_pool* p, const IoSet& ios, int32_t n, DevPlanShape& sh,
+                          DevPlanWs& w) {
+  if (p->dtype != LORA_F16 && p->dtype != LORA_BF16)
+    return fail(LORA_E_UNSUPPORTED, "device-planned decode needs 16-bit pages (use lora_bgmv_apply)");
+  if (p->P / p->rs_of(p->max_rank) < 16)
+    return fail(LORA_E_UNSUPPORTED, "device-planned decode needs >= 16 B rows per page");
+  if (n > kDpMaxTokens) return fail(LORA_E_ARG, "%d tokens exceed %d per device-planned call", n, kDpMaxTokens);
+  if (p->max_adapters > (1 << 21)) return fail(LORA_E_UNSUPPORTED, "max_adapters above 2^21");
+  memset(&sh, 0, sizeof(sh));
+  sh.n = n;
+  sh.J = ios.n_io;
+  sh.G = ((2 * p->n_cu + 7) / 8) * 8;
+  if (sh.G > kDpMaxBlocks) sh.G = kDpMaxBlocks;
+  sh.rs_per16 = 16 / p->elt;
+  sh.cap = n;
+  sh.ov_s = (int32_t)kPieceSetupShrink;
+  sh.ov_e = (int32_t)kPieceSetupExpand;
+  for (int j = 0; j < ios.n_io; ++j) {
+    if (ios.io[j].npa > kMaxNpa)
+      return fail(LORA_E_UNSUPPORTED, "io %d: A rows span more than %d pages", j, kMaxNpa);
+    sh.slice[j] = ios.io[j].slice;
+    sh.nst[j] = (ios.io[j].d_in + 63) / 64;
+    sh.nch[j] = (ios.io[j].d_out + 63) / 64;
+  }
+  if (!devplan_ws(sh.J, n, sh.G, p->max_rank, w))
+    return fail(LORA_E_ARG, "partial tiles exceed 2^31 float4 units");
+  return LORA_OK;
+}
+
 }  // namespace
 
 #define LORA_TRY(expr)          \
@@ -178,6 +210,50 @@ lora_status lora_bgmv_apply(lora_pool* p, int32_t n_io, const lora_io* io, const
   LORA_TRY(check_pool(p));
   return hip_status(launch_bgmv_apply(p->types(y_dtype), p->view(), ios, ids, n, (hipStream_t)stream),
                     "bgmv_apply");
+}
+
+lora_status lora_bgmv_planned_workspace_size(lora_pool* p, int32_t n_io, const lora_io* io,
+                                             int32_t n, size_t* bytes) {
+  clear_error();
+  if (!p || !bytes) return fail(LORA_E_ARG, "null argument");
+  if (n_io < 1 || n_io > LORA_MAX_IO || !io) return fail(LORA_E_ARG, "n_io must be in [1, %d]", LORA_MAX_IO);
+  if (n < 0) return fail(LORA_E_ARG, "n < 0");
+  IoSet ios;
+  memset(&ios, 0, sizeof(ios));
+  ios.n_io = n_io;
+  for (int k = 0; k < n_io; ++k) {
+    LORA_TRY(check_slice(p, io[k].slice));
+    ios.io[k] = p->io(io[k].slice, nullptr, nullptr);
+  }
+  DevPlanShape sh;
+  DevPlanWs w;
+  LORA_TRY(devplan_shape(p, ios, n, sh, w));
+  *bytes = w.bytes;
+  return LORA_OK;
+}
+
+lora_status lora_bgmv_apply_planned(lora_pool* p, int32_t n_io, const lora_io* io,
+                                    const int32_t* ids, int32_t n, int32_t y_dtype, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!p) return fail(LORA_E_ARG, "null pool");
+  LORA_TRY(check_ydt(p, y_dtype));
+  IoSet ios;
+  LORA_TRY(build_ioset(p, n_io, io, ios));
+  if (n < 0) return fail(LORA_E_ARG, "n < 0");
+  if (n == 0) return LORA_OK;
+  if (!ids) return fail(LORA_E_ARG, "null ids");
+  DevPlanShape sh;
+  DevPlanWs w;
+  LORA_TRY(devplan_shape(p, ios, n, sh, w));
+  if (!ws || ws_bytes < w.bytes)
+    return fail(LORA_E_ARG, "workspace of %zu bytes, this call needs %zu (lora_bgmv_planned_workspace_size)",
+                ws_bytes, w.bytes);
+  if ((uintptr_t)ws & 255u) return fail(LORA_E_ARG, "workspace not 256-byte aligned");
+  LORA_TRY(check_pool(p));
+  return hip_status(launch_devplan_apply(p->types(y_dtype), p->view(), ios, ids, sh, w,
+                                         reinterpret_cast<char*>(ws), (hipStream_t)stream),
+                    "bgmv_apply_planned");
 }
 
 lora_status lora_sgmv_shrink(lora_pool* p, const lora_plan* pl, int32_t slice, const void* x,

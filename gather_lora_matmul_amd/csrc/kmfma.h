@@ -296,9 +296,14 @@ __device__ __forceinline__ void shrink_stages(const PoolView& pv, const DevEntry
 __device__ __forceinline__ float4* part_at(const PlanView& pl, int32_t off) {
   return reinterpret_cast<float4*>(pl.part) + off;
 }
-// Contributions [c_off[0], c_off[1]) of tile i in launch slice j.
-__device__ __forceinline__ const int32_t* contrib_range(const PlanView& pl, int j, int i) {
-  return pl.c_off + (int64_t)j * (pl.n_mfma + 1) + i;
+// Tiles per launch slice: the plan's count, or, for a plan built on the
+// device, the count the planner wrote.
+__device__ __forceinline__ int plan_tiles(const PlanView& pl) {
+  return pl.n_tiles_dev ? *pl.n_tiles_dev : pl.n_mfma;
+}
+// Contributions [c_off[0], c_off[1]) of tile i in launch slice j (T tiles).
+__device__ __forceinline__ const int32_t* contrib_range(const PlanView& pl, int T, int j, int i) {
+  return pl.c_off + (int64_t)j * (T + 1) + i;
 }
 // Unit u of a partial tile with ntb token blocks -> (slot, first rank)
 __device__ __forceinline__ int unit_slot(int u, int ntb) { return 16 * ((u >> 6) % ntb) + (u & 15); }
@@ -373,13 +378,17 @@ __device__ __forceinline__ void shrink_range(const PoolView& pv, const PlanView&
   const cptr fl = (cptr)(pl.part_fl + L);
   const int32_t part_first = fl[0], part_last = fl[1];
   int* toks = reinterpret_cast<int*>(lb.misc + kOffToks);
-  for_each_piece(pl.bs_shrink, L, pl.n_mfma, [&](int j) { return (io_of(j).d_in + kKC - 1) / kKC; },
+  const int ntl = plan_tiles(pl);
+  for_each_piece(pl.bs_shrink, L, ntl, [&](int j) { return (io_of(j).d_in + kKC - 1) / kKC; },
                  [&](int j, int i, int k0, int k1, bool first, bool last) {
     const IoDesc io = io_of(j);
     const int nst = (io.d_in + kKC - 1) / kKC;
     const PlanItem item = pl.items[i];
     const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
-    const int32_t part_off = first ? part_first : last ? part_last : pl.c_ent[*contrib_range(pl, j, i)];
+    // (device-built plans: an adapter not resident in this slice has no work
+    // here, and the expand skips the same piece)
+    if (e.rank <= 0) return;
+    const int32_t part_off = first ? part_first : last ? part_last : pl.c_ent[*contrib_range(pl, ntl, j, i)];
     load_tile_tokens(pl, item, toks);
     {  // A page ids of the tile's rank rows (rows past the rank repeat the last)
       int* apg = reinterpret_cast<int*>(lb.misc + kOffApg);
@@ -408,7 +417,7 @@ __device__ __forceinline__ void shrink_range(const PoolView& pv, const PlanView&
 // partial tiles in block order (the first one, then += the others).
 __device__ __forceinline__ void shrink_reduce_tile(const PlanView& pl, const IoDesc& io, int tile,
                                                    int rank, float* v, int v_ld, int* toks) {
-  const int32_t* off = contrib_range(pl, 0, tile);
+  const int32_t* off = contrib_range(pl, pl.n_mfma, 0, tile);
   const int c0 = off[0], c1 = off[1];
   if (c1 - c0 <= 1) return;  // a single block covered the tile and wrote v
   const PlanItem item = pl.items[tile];
@@ -818,13 +827,15 @@ __device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView&
   uint16_t* Vh = reinterpret_cast<uint16_t*>(lb.a);
   uint16_t* Vl = reinterpret_cast<uint16_t*>(lb.b);
   float* Ds = reinterpret_cast<float*>(lb.c);
-  for_each_piece(pl.bs_expand, L, pl.n_mfma, [&](int j) { return (io_of(j).d_out + 63) / 64; },
+  const int ntl = plan_tiles(pl);
+  for_each_piece(pl.bs_expand, L, ntl, [&](int j) { return (io_of(j).d_out + 63) / 64; },
                  [&](int j, int i, int c0, int c1, bool, bool) {
     const IoDesc io = io_of(j);
     const PlanItem item = pl.items[i];
     const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
+    if (e.rank <= 0) return;  // not resident in this slice: y untouched
     load_tile_tokens(pl, item, toks);
-    const int32_t* off = contrib_range(pl, j, i);
+    const int32_t* off = contrib_range(pl, ntl, j, i);
     const int cb0 = off[0], cb1 = off[1];
     __syncthreads();
     switch ((e.rs + 31) >> 5) {

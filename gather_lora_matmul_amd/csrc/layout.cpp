@@ -129,10 +129,44 @@ void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n
   }
 }
 
+void spread_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G, int64_t ov,
+                   int32_t* out) {
+  const int T = (int)w.size(), J = (int)n.size();
+  int64_t per = 0, units = 0;
+  for (int32_t x : w) per += x;
+  for (int32_t nj : n) units += nj;
+  const int64_t total = per * units + ov * J * T;
+  int j = 0, t = 0;
+  int64_t b = 0;  // start of tile t of slice j, the set-ups of the tiles before it included
+  for (int L = 0; L <= G; ++L) {
+    const int64_t target = total * L / G;
+    set_pos(out, L, J, 0, 0);
+    while (j < J) {
+      const int64_t wt = w[(size_t)t];
+      const int64_t nj = n[(size_t)j];
+      // unit 0 starts at b, unit k >= 1 at b + ov + k wt
+      int64_t k = 0;
+      if (target > b) {
+        k = 1;
+        while (k < nj && b + ov + k * wt < target) ++k;
+      }
+      if (k < nj) {
+        set_pos(out, L, j, t, (int)k);
+        break;
+      }
+      b += ov + wt * nj;
+      if (++t == T) {
+        t = 0;
+        ++j;
+      }
+    }
+  }
+}
+
 bool layout_host(const std::vector<int32_t>& ws, const std::vector<int32_t>& we,
                  const std::vector<int32_t>& tu, const std::vector<int32_t>& nst,
                  const std::vector<int32_t>& nch, int G, int64_t ov_s, int64_t ov_e,
-                 LayoutHost& h) {
+                 LayoutHost& h, bool spread) {
   const int J = (int)nst.size();
   const int T = (int)ws.size();
   h.o_bs = 0;
@@ -142,8 +176,13 @@ bool layout_host(const std::vector<int32_t>& ws, const std::vector<int32_t>& we,
   h.o_ent = (h.o_off + (size_t)J * ((size_t)T + 1) + 3) & ~(size_t)3;
   std::vector<int32_t>& buf = h.buf;
   buf.assign(h.o_ent, 0);
-  balance_ranges(ws, nst, G, ov_s, buf.data() + h.o_bs);
-  balance_ranges(we, nch, G, ov_e, buf.data() + h.o_be);
+  if (spread) {
+    spread_ranges(ws, nst, G, ov_s, buf.data() + h.o_bs);
+    spread_ranges(we, nch, G, ov_e, buf.data() + h.o_be);
+  } else {
+    balance_ranges(ws, nst, G, ov_s, buf.data() + h.o_bs);
+    balance_ranges(we, nch, G, ov_e, buf.data() + h.o_be);
+  }
   // per (j, tile) the blocks whose shrink ranges meet it, in block order; each
   // block's first and last piece
   std::vector<std::vector<int32_t>> lists((size_t)J * (size_t)T);

@@ -26,6 +26,13 @@ constexpr int kPosInts = 4;
 constexpr int64_t kMaxPiecesOv = 16384;
 void balance_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G, int64_t ov,
                     int32_t* out);
+// Block L's range starts at the first unit whose start is at or past
+// total * L / G, where every tile adds its set-up ov before its unit 0 (unit 0
+// of a tile spans the set-up and its own weight; total counts all units and
+// set-ups).  Every boundary is independent of the others (the device planner
+// cuts its ranges this way); with ov == 0 it is balance_ranges' plain split.
+void spread_ranges(const std::vector<int32_t>& w, const std::vector<int32_t>& n, int G, int64_t ov,
+                   int32_t* out);
 
 // The int32 image of a launch shape's layout, copied to the device as is:
 //   [o_bs]  shrink ranges, (G + 1) positions (stage units, weights ws)
@@ -44,9 +51,10 @@ struct LayoutHost {
 
 // ov_s, ov_e: per-piece set-up cost of the shrink and expand ranges (in the
 // units of ws, we).  False if the partial tiles would exceed 2^31 float4 units.
+// spread: cut the ranges with spread_ranges instead of balance_ranges.
 bool layout_host(const std::vector<int32_t>& ws, const std::vector<int32_t>& we,
                  const std::vector<int32_t>& tu, const std::vector<int32_t>& nst,
                  const std::vector<int32_t>& nch, int G, int64_t ov_s, int64_t ov_e,
-                 LayoutHost& h);
+                 LayoutHost& h, bool spread = false);
 
 }  // namespace lora

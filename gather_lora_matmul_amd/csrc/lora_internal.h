@@ -73,6 +73,36 @@ constexpr int kShortG = 4;   // tokens per short item
 constexpr int kTileM = 64;   // tokens per MFMA tile
 constexpr int kMaxNpa = 8;            // MFMA tiles: pages per A row, at most
 
+// Cost weights of one MFMA tile of `count` tokens whose adapter has rank
+// `rmax` (largest over the slices; stored B rows of `rs` elements), for the
+// persistent kernels' block ranges, and the size of one of its partial tiles.
+// Used by the host planner and by the device planner alike.
+struct TileCost {
+  int32_t ws;  // one shrink stage (64 columns of d_in), units of ~8 ns
+  int32_t we;  // one expand chunk (64 rows of d_out), units of ~4 ns
+  int32_t tu;  // float4 units of a partial tile
+};
+// Set-up of one tile piece of a block range, in the weight units of TileCost
+// (measured: ~5 us for a shrink piece -- tokens, A page ids, pipeline fill --
+// and ~6 us for an expand piece -- tokens, V from the partial tiles, fill).
+constexpr int64_t kPieceSetupShrink = 600;
+constexpr int64_t kPieceSetupExpand = 1800;
+__host__ __device__ inline TileCost tile_cost(int count, int rmax, int rs) {
+  const int rp = (rmax + 15) / 16 * 16;
+  const int tb = (count + 15) / 16;  // 16-token blocks
+  // a stage costs about one memory round trip whatever it moves: a large
+  // fixed part plus half the 128-byte rows it loads
+  const int ws = 64 + (16 * tb + rp) / 2;
+  // an expand chunk, from per-chunk times measured on MI355X: tiles of more
+  // than 16 tokens take 64-row steps, ~141 + 60 NK + 2 count; tiles of at
+  // most 16 tokens take wide steps (4 or 2 chunks, B of several chunks per
+  // round trip), ~51 + 51 NK + count per chunk (NK = 32-column k steps of the
+  // stored B row)
+  const int nk = (rs + 31) / 32;
+  const int we = count <= 16 ? 51 + 51 * nk + count : 141 + 60 * nk + 2 * count;
+  return TileCost{ws, we, (rp / 16) * tb * 64};
+}
+
 // Element types of one call: pages (w), activations x (x) and y (y), as
 // lora_dtype codes.  x equals w except on FP8 pools (16-bit x).
 struct Types {
@@ -131,6 +161,9 @@ struct PlanView {
   const int32_t* c_off;        // [n_io][n_mfma + 1]
   const int32_t* c_ent;
   float* part;                 // partial tiles
+  // Plans built on the device: the tile count as the planner wrote it (the
+  // host knows only a bound, in n_mfma); null for host-built plans.
+  const int32_t* n_tiles_dev;
   int32_t n_items;
   int32_t n_tokens;
   int32_t n_mfma;

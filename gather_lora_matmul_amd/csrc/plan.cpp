@@ -22,12 +22,6 @@ static_assert(sizeof(RangePos) == kPosInts * sizeof(int32_t), "device positions 
 
 namespace lora {
 
-// Set-up of one tile piece of a block range, in the weight units below
-// (measured: ~5 us for a shrink piece -- tokens, A page ids, pipeline fill --
-// and ~6 us for an expand piece -- tokens, V from the partial tiles, fill).
-constexpr int64_t kPieceSetupShrink = 600;
-constexpr int64_t kPieceSetupExpand = 1800;
-
 std::vector<int32_t> layout_key(const IoSet& ios) {
   std::vector<int32_t> key;
   key.push_back(ios.n_io);
@@ -291,18 +285,10 @@ lora_status lora_plan_build(lora_plan* pl, const int32_t* ids, int32_t n, int32_
       const PlanItem& it = pl->h_items[(size_t)i];
       int rmax = 0;
       for (int s = 0; s < p->n_slices; ++s) rmax = std::max(rmax, p->slot(s, it.adapter).rank);
-      const int rp = (rmax + 15) / 16 * 16;
-      // a stage costs about one memory round trip whatever it moves: a large
-      // fixed part plus half the 128-byte rows it loads (units of ~8 ns)
-      ws[(size_t)i] = 64 + (16 * ((it.count + 15) / 16) + rp) / 2;
-      // an expand chunk (64 output rows), from per-chunk times measured on
-      // MI355X in units of ~4 ns: tiles of more than 16 tokens take 64-row
-      // steps, ~141 + 60 NK + 2 count; tiles of at most 16 tokens take wide
-      // steps (4 or 2 chunks, B of several chunks per round trip), ~51 + 51 NK
-      // + count per chunk (NK = 32-column k steps of the stored B row)
-      const int nk = (p->rs_of(rmax) + 31) / 32;
-      we[(size_t)i] = it.count <= 16 ? 51 + 51 * nk + it.count : 141 + 60 * nk + 2 * it.count;
-      tu[(size_t)i] = (rp / 16) * ((it.count + 15) / 16) * 64;
+      const TileCost tc = tile_cost(it.count, rmax, p->rs_of(rmax));
+      ws[(size_t)i] = tc.ws;
+      we[(size_t)i] = tc.we;
+      tu[(size_t)i] = tc.tu;
     }
   }
   pl->n_tokens = n;

@@ -218,6 +218,7 @@ struct lora_plan {
     v.c_off = lay ? lay->d_buf + lay->o_off : nullptr;
     v.c_ent = lay ? lay->d_buf + lay->o_ent : nullptr;
     v.part = reinterpret_cast<float*>(part);
+    v.n_tiles_dev = nullptr;
     v.n_items = n_items;
     v.n_tokens = n_tokens;
     v.n_mfma = n_mfma;

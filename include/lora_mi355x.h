@@ -345,6 +345,37 @@ lora_status lora_apply_noalloc(lora_pool* pool, const lora_plan* plan, int32_t n
                                const lora_io* io_host, int32_t y_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode with device ids, grouped on the device (S-LoRA paper explainer,
+ * section "BGMVカーネル": one launch sequence for a batch whose tokens carry
+ * their own adapters and ranks; multi-LoRA serving article, SGMV section: the
+ * index vector sends tokens to adapters, tokens of one adapter form one
+ * segment).
+ * ------------------------------------------------------------------------- */
+/* Bytes of caller-owned device workspace that lora_bgmv_apply_planned needs
+ * for n tokens over the slices of io (only io[k].slice is read): the plan and
+ * a bound on its split-K partial tiles (about 10 MB for 256 tokens, two
+ * slices, rank <= 64).  LORA_E_UNSUPPORTED on pools the MFMA tiles cannot
+ * take (FP8 or fp32 pages, fewer than 16 B rows per page, A rows over more
+ * than 8 pages). */
+lora_status lora_bgmv_planned_workspace_size(lora_pool* pool, int32_t n_io,
+                                             const lora_io* io_host, int32_t n,
+                                             size_t* bytes);
+/* y_i += s_a B_a (A_a x_i) for every token i of the slices of io, like
+ * lora_bgmv_apply, with ids_dev [n] on the device (ids outside [0,
+ * max_adapters): the token is skipped; an adapter not resident in a slice
+ * leaves that slice's row untouched).  One workgroup sorts the tokens by
+ * adapter into tiles of at most 64 tokens and lays out the block ranges of
+ * the planned MFMA kernels in the workspace, then the fused shrink and expand
+ * launches run from it: three launches on `stream`, no host wait, no
+ * allocation (graph-capturable).  n <= 1024; 16-bit pools only.  workspace_dev:
+ * 256-byte aligned, at least lora_bgmv_planned_workspace_size bytes (else
+ * LORA_E_ARG), no initial contents; calls sharing a workspace must not
+ * overlap. */
+lora_status lora_bgmv_apply_planned(lora_pool* pool, int32_t n_io, const lora_io* io_host,
+                                    const int32_t* ids_dev, int32_t n, int32_t y_dtype,
+                                    void* workspace_dev, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Debug / verification of the page-table resolution done inside the kernels.
  * ------------------------------------------------------------------------- */
 /* For token i: a_off[i][k*npa + c] = byte offset (from the pool base) of page

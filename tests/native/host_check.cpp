@@ -11,6 +11,7 @@
 #include <random>
 #include <vector>
 
+#include "devplan.h"
 #include "lora_internal.h"
 
 namespace lora {
@@ -35,6 +36,8 @@ hipError_t launch_sgmv_shrink(const Types&, const PoolView&, const PlanView&, co
 hipError_t launch_sgmv_expand(const Types&, const PoolView&, const PlanView&, const IoDesc&,
                               const float*, int32_t, hipStream_t) STUB()
 hipError_t launch_apply(const Types&, const PoolView&, const PlanView&, const IoSet&, hipStream_t) STUB()
+hipError_t launch_devplan_apply(const Types&, const PoolView&, const IoSet&, const int32_t*,
+                                const DevPlanShape&, const DevPlanWs&, char*, hipStream_t) STUB()
 hipError_t launch_debug_decode(int, const void*, int64_t, float*, hipStream_t) STUB()
 hipError_t launch_debug_resolve(const PoolView&, const IoDesc&, int32_t, int, const int32_t*, int32_t,
                                 int64_t*, int64_t*, hipStream_t) STUB()

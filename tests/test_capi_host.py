@@ -383,3 +383,44 @@ def test_x_group_needs_one_x_and_one_d_in():
         assert lib.lora_bgmv_apply(sp.handle, 2, io, a, 4, L.LORA_BF16, None) == -1
         io = (L.Io * 3)(L.Io(0, 1, a, a), L.Io(2, 0, b, b), L.Io(1, 1, a, b))
         assert lib.lora_bgmv_apply(sp.handle, 3, io, a, 4, L.LORA_BF16, None) == -5  # valid: pool state
+
+
+def test_device_planned_decode_arguments():
+    # lora_bgmv_apply_planned: the workspace bound grows with tokens and
+    # slices; pools the MFMA tiles cannot take, more than 1024 tokens and a
+    # short or misaligned workspace are refused before anything runs
+    wl = W.small_workload("bf16", 1024, 1000, [8, 40, 16, 64, 24], 1024, n_slices=3, seed=21)
+    sp = _host_pool(wl)
+    try:
+        n1 = L.lora_bgmv_planned_workspace_size(sp.handle, [0], 64)
+        n2 = L.lora_bgmv_planned_workspace_size(sp.handle, [0, 2], 64)
+        n3 = L.lora_bgmv_planned_workspace_size(sp.handle, [0, 2], 256)
+        assert 0 < n1 < n2 < n3 and n3 % 256 == 0
+        with pytest.raises(L.LoraError) as e:
+            L.lora_bgmv_planned_workspace_size(sp.handle, [0], 1025)
+        assert e.value.status == -1
+        with pytest.raises(L.LoraError) as e:
+            L.lora_bgmv_planned_workspace_size(sp.handle, [3], 8)
+        assert e.value.status == -1
+        fake = 1 << 20  # never dereferenced: every call below fails on the host
+        io = (L.Io * 2)(L.Io(0, 0, fake, fake), L.Io(2, 0, fake, fake))
+        lib = L.lib()
+        st = lib.lora_bgmv_apply_planned(sp.handle, 2, io, fake, 64, L.LORA_BF16, fake, n2 - 256, None)
+        assert st == -1 and "workspace" in L.lora_last_error()
+        st = lib.lora_bgmv_apply_planned(sp.handle, 2, io, fake, 64, L.LORA_BF16, fake + 16, n2, None)
+        assert st == -1 and "aligned" in L.lora_last_error()
+        st = lib.lora_bgmv_apply_planned(sp.handle, 2, io, fake, 64, L.LORA_BF16, fake, n2, None)
+        assert st == -5 and "host-only" in L.lora_last_error()
+        assert lib.lora_bgmv_apply_planned(sp.handle, 2, io, fake, 0, L.LORA_BF16, None, 0, None) == 0
+    finally:
+        sp.close()
+    # pages the MFMA tiles cannot take: fp32, FP8, fewer than 16 B rows per page
+    for args in [("f32", 256, 256, [4, 8], 256), ("e4m3", 256, 256, [8, 16], 256),
+                 ("bf16", 512, 512, [8, 64], 512)]:
+        sp = _host_pool(W.small_workload(*args))
+        try:
+            with pytest.raises(L.LoraError) as e:
+                L.lora_bgmv_planned_workspace_size(sp.handle, [0], 8)
+            assert e.value.status == -7, args
+        finally:
+            sp.close()

@@ -5,6 +5,8 @@ recovery, and runs:
   * the fp64 oracle's C entry points (tests/native/oracle_check.c);
   * the block-range layout of the MFMA kernels (layout.cpp with
     tests/native/layout_check.cpp);
+  * the device planner run on the host (devplan.h with
+    tests/native/devplan_check.cpp);
   * the library's host paths -- pool, page table, planner, launch-shape
     preparation, argument checks (pool.cpp, plan.cpp, api.cpp, layout.cpp with
     tests/native/host_check.cpp, kernels stubbed out: host-only pools never
@@ -51,6 +53,16 @@ def test_layout_under_sanitizers(tmp_path):
     _run([cxx, "-std=c++17", "-I" + CSRC] + SAN +
          [os.path.join(NATIVE, "layout_check.cpp"), os.path.join(CSRC, "layout.cpp"), "-o", exe])
     print(_run([exe, "300"]))
+
+
+def test_device_planner_under_sanitizers(tmp_path):
+    cxx = shutil.which("g++")
+    if not cxx or not os.path.isdir(ROCM_INC):
+        pytest.skip("no g++ or ROCm headers")
+    exe = str(tmp_path / "devplan_check")
+    _run([cxx, "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I" + ROCM_INC, "-I" + CSRC] + SAN +
+         [os.path.join(NATIVE, "devplan_check.cpp"), os.path.join(CSRC, "layout.cpp"), "-o", exe])
+    print(_run([exe, "150"]))
 
 
 def test_host_library_paths_under_sanitizers(tmp_path):
