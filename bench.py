@@ -104,7 +104,8 @@ def measured_traffic(workload: str, entry: str, src_hash: str, path: str = None)
 STEP_KERNELS = {"lora_bgmv_apply": ("lora::k_bgmv_apply",),
                 "lora_apply": ("lora::k_apply_", "lora::k_sgmv_", "lora::k_short_"),
                 "lora_bgmv_shrink+expand": ("lora::k_bgmv_shrink", "lora::k_bgmv_expand"),
-                "lora_sgmv_shrink+expand": ("lora::k_sgmv_", "lora::k_apply_", "lora::k_short_")}
+                "lora_sgmv_shrink+expand": ("lora::k_sgmv_", "lora::k_apply_", "lora::k_short_"),
+                "lora_bgmv_apply_planned": ("k_devplan", "lora::k_apply_")}
 COPY_BYTES = 64 << 20  # the --copy-calib copy
 
 

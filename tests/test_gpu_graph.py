@@ -100,3 +100,58 @@ def test_graph_planned_apply_mfma_and_short_items():
         torch.cuda.synchronize()
         L.lora_plan_destroy(plan)
         sp.close()
+
+
+def test_graph_device_planned_decode():
+    # the device planner, then the MFMA launches, all from the workspace: the
+    # captured graph replays the whole sequence; the ids are changed between
+    # replays (the graph reads them at replay time), and every replay gives the
+    # bits of an eager call on the same ids
+    wl = W.small_workload("bf16", 1024, 1000, [8, 40, 16, 64, 24], 1024, n_slices=2, seed=33)
+    rng = np.random.default_rng(5)
+    ids_a = rng.integers(-1, 5, 200).astype(np.int32)
+    ids_b = rng.integers(0, 5, 200).astype(np.int32)
+    ids_b[:90] = 3
+    log("[case] graph capture: lora_bgmv_apply_planned, 200 tokens, ids changed between replays")
+    sp = SyntheticPool(wl)
+    try:
+        ba = W.custom_batch(wl, ids_a, zero_y0=False)
+        bb = W.custom_batch(wl, ids_b, zero_y0=False)
+        ids = ids_tensor(ids_a)
+        xs = [to_device(ba.x[s], "bf16") for s in range(2)]
+        y0s = [to_device(ba.y0[s], "bf16") for s in range(2)]
+        ys = [y.clone() for y in y0s]
+        ws = torch.empty(L.lora_bgmv_planned_workspace_size(sp.handle, [0, 1], 200), dtype=torch.uint8,
+                         device="cuda")
+        call = L.prepare_bgmv_apply_planned(sp.handle, [(s, xs[s], ys[s]) for s in range(2)], ids,
+                                            L.LORA_BF16, ws)
+        eager = {}
+        for key, idv in (("a", ids_a), ("b", ids_b)):
+            ids.copy_(torch.from_numpy(idv))
+            for y, y0 in zip(ys, y0s):
+                y.copy_(y0)
+            call(torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            eager[key] = [y.clone() for y in ys]
+        bref = W.Batch(ids=ids_b, x=ba.x, y0=ba.y0)
+        check_all(wl, bref, {s: from_device(eager["b"][s], "bf16") for s in range(2)}, {}, [0, 1],
+                  "bf16", "graph devplan eager")
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            call(torch.cuda.current_stream().cuda_stream)
+        for k in range(6):
+            key = "ab"[k % 2]
+            ids.copy_(torch.from_numpy(ids_a if key == "a" else ids_b))
+            for y, y0 in zip(ys, y0s):
+                y.copy_(y0)
+            g.replay()
+            junk = (torch.randn(4096, device="cuda") * 2).sum()  # eager work between replays
+            torch.cuda.synchronize()
+            for j in range(2):
+                assert torch.equal(ys[j].view(torch.int16), eager[key][j].view(torch.int16)), \
+                    "replay %d (ids %s) slice %d" % (k, key, j)
+        del bb, junk
+    finally:
+        torch.cuda.synchronize()
+        sp.close()
