@@ -176,6 +176,7 @@ __host__ __device__ inline void dp_rank_sort(Ctx& cx, const uint32_t* a, uint32_
     const uint32_t v = a[i];
     const int g1 = (r + 1) * per < q4 ? (r + 1) * per : q4;
     int below = 0;
+#pragma unroll 8
     for (int g = r * per; g < g1; ++g) {
       const uint4 q = a4[g];
       below += (q.x < v) + (q.y < v) + (q.z < v) + (q.w < v);
@@ -203,7 +204,10 @@ __host__ __device__ inline void dp_range_start(int L, int G, int J, int T, const
                                                int64_t ov, int32_t& seq, int32_t& k) {
   int64_t units = 0;
   for (int j = 0; j < J; ++j) units += n[j];
-  const int64_t target = (per * units + ov * J * T) * L / G;
+  const int64_t num = (per * units + ov * J * T) * L;
+  int lg = 0;  // the grid is a power of two in practice: a shift instead of a 64-bit division
+  while ((1 << lg) < G) ++lg;
+  const int64_t target = (1 << lg) == G ? num >> lg : num / G;
   // the slice: the first whose last unit starts at or past target
   int j = 0;
   int64_t sj = 0;  // start of slice j, set-ups included

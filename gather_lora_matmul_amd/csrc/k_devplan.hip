@@ -36,7 +36,8 @@ struct DpDeviceCtx {
     if (lane == 63) wtot[w] = v;
     dp_barrier();
     int add = 0;
-    for (int q = 0; q < w; ++q) add += wtot[q];
+#pragma unroll
+    for (int q = 0; q < kDpThreads / 64; ++q) add += q < w ? wtot[q] : 0;
     if (t < n) a[t] = v + add;
     dp_barrier();
   }
