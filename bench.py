@@ -47,9 +47,9 @@ DEVPLAN_SOURCES = ("k_devplan.hip", "devplan.h", "k_sgmv.hip", "kmfma.h", "kcomm
                    "lora_internal.h")
 
 
-def entry_of(planned: bool, devplan: bool, mode: str) -> str:
+def entry_of(planned: bool, devplan: bool, mode: str, reuse: bool = False) -> str:
     if devplan:
-        return "lora_bgmv_apply_planned"
+        return "lora_dplan_apply" if reuse else "lora_bgmv_apply_planned"
     if mode == "fused":
         return "lora_apply" if planned else "lora_bgmv_apply"
     return "lora_sgmv_shrink+expand" if planned else "lora_bgmv_shrink+expand"
@@ -105,7 +105,8 @@ STEP_KERNELS = {"lora_bgmv_apply": ("lora::k_bgmv_apply",),
                 "lora_apply": ("lora::k_apply_", "lora::k_sgmv_", "lora::k_short_"),
                 "lora_bgmv_shrink+expand": ("lora::k_bgmv_shrink", "lora::k_bgmv_expand"),
                 "lora_sgmv_shrink+expand": ("lora::k_sgmv_", "lora::k_apply_", "lora::k_short_"),
-                "lora_bgmv_apply_planned": ("k_devplan", "lora::k_apply_")}
+                "lora_bgmv_apply_planned": ("k_devplan", "lora::k_apply_"),
+                "lora_dplan_apply": ("lora::k_apply_",)}
 COPY_BYTES = 64 << 20  # the --copy-calib copy
 
 
@@ -221,11 +222,14 @@ class Runner:
     workspaces, and the step that applies one batch."""
 
     def __init__(self, name: str, mode: str = "fused", planned: bool = False, n_batches=None,
-                 l_long: int = 0, qkv=None, n_tokens=None, devplan: bool = False):
+                 l_long: int = 0, qkv=None, n_tokens=None, devplan: bool = False,
+                 reuse: bool = False):
         """qkv: None, or "separate" / "shared": q, k and v (slices 0-2) reading
         one x buffer, without or with an x_group (decode BGMV only).  devplan:
         decode workloads through lora_bgmv_apply_planned (tokens grouped by
-        adapter on the device)."""
+        adapter on the device); with reuse, each rotating batch's device plan is
+        built once before timing and a step is lora_dplan_apply alone (the cost
+        of every further layer that shares a decode step's ids)."""
         import torch
 
         import gather_lora_matmul_amd as L
@@ -236,6 +240,7 @@ class Runner:
         self.wl = wl = W.make_workload(cfg)
         self.planned = planned or cfg in (3, 4)
         self.devplan = devplan and not self.planned
+        self.reuse = self.devplan and reuse
         if self.devplan:
             mode = "fused"
         self.mode = mode
@@ -284,7 +289,14 @@ class Runner:
         # fused steps: arguments checked and marshalled once per rotating batch
         self.calls = []
         self.ws_dev = None
-        if self.devplan:
+        self.dplans = []
+        if self.reuse:
+            for k, b in enumerate(self.batches):
+                d = L.lora_dplan_create(self.sp.handle, len(b.ids), slices)
+                L.lora_dplan_build(d, slices, self.ids_d[k])
+                self.dplans.append(d)
+            torch.cuda.synchronize()
+        elif self.devplan:
             n_max = max(len(b.ids) for b in self.batches)
             self.ws_dev = torch.empty(L.lora_bgmv_planned_workspace_size(self.sp.handle, slices, n_max),
                                       dtype=torch.uint8, device="cuda")
@@ -294,13 +306,15 @@ class Runner:
                 io = [(s, self.xs[k][j], self.ys[k][j], group) for j, s in enumerate(slices)]
                 if self.planned:
                     c = L.prepare_apply(self.sp.handle, self.plans[k], io, self.ydt, workspace=self.wss[k])
+                elif self.reuse:
+                    c = L.prepare_dplan_apply(self.sp.handle, self.dplans[k], io, len(b.ids), self.ydt)
                 elif self.devplan:
                     c = L.prepare_bgmv_apply_planned(self.sp.handle, io, self.ids_d[k], self.ydt,
                                                      self.ws_dev)
                 else:
                     c = L.prepare_bgmv_apply(self.sp.handle, io, self.ids_d[k], self.ydt)
                 self.calls.append(c)
-        self.entry = entry_of(self.planned, self.devplan, mode)
+        self.entry = entry_of(self.planned, self.devplan, mode, self.reuse)
         self.src_hash = source_hash(sources_of(self.planned, self.devplan))
 
     def step(self, i: int):
@@ -370,6 +384,9 @@ class Runner:
         for p in self.plans:
             self.L.lora_plan_destroy(p)
         self.plans = []
+        for d in self.dplans:
+            self.L.lora_dplan_destroy(d)
+        self.dplans = []
         self.sp.close()
 
 
@@ -492,6 +509,8 @@ def main():
     ap.add_argument("--devplan", action="store_true",
                     help="decode workloads: group the tokens by adapter on the device "
                          "(lora_bgmv_apply_planned) instead of lora_bgmv_apply")
+    ap.add_argument("--reuse-plan", action="store_true",
+                    help="with --devplan: build each batch's device plan once, time lora_dplan_apply")
     ap.add_argument("--l-long", type=int, default=0,
                     help="planned batches: groups shorter than this run as short VALU items "
                          "(0: every group of a 16-bit pool is an MFMA tile)")
@@ -514,7 +533,7 @@ def main():
         cfg = WORKLOADS[args.workload]
         planned = args.planned or cfg in (3, 4)
         devplan = args.devplan and not planned
-        entry = entry_of(planned, devplan, args.mode)
+        entry = entry_of(planned, devplan, args.mode, args.reuse_plan)
         rec = record_traffic(args.record_traffic[0], args.record_traffic[1], args.workload, entry,
                              source_hash(sources_of(planned, devplan)), args.command)
         print(json.dumps({"workload": args.workload, "entry": entry,
@@ -529,7 +548,7 @@ def main():
     import torch
     torch.cuda.set_device(0)
     head = Runner(args.workload, args.mode, args.planned, args.batches, args.l_long,
-                  n_tokens=args.tokens, devplan=args.devplan)
+                  n_tokens=args.tokens, devplan=args.devplan, reuse=args.reuse_plan)
     rec = head.record(args.steps, args.warmup)
     wl = head.wl
     cfg = WORKLOADS[args.workload]
@@ -581,17 +600,19 @@ def main():
                                              ("llama7b_decode_bgmv_fp8", False, None, None, False),
                                              ("hetero_decode_bgmv", False, None, None, False),
                                              ("hetero_decode_bgmv", False, None, None, True),
+                                             ("hetero_decode_bgmv", False, None, None, "reuse"),
                                              ("hetero_decode_bgmv", True, None, None, False),
                                              ("llama13b_prefill_sgmv", True, None, None, False),
                                              ("llama70b_mixed_apply", True, None, None, False)):
             key = name + ("/planned" if planned and WORKLOADS[name] in (1, 2) else "")
-            key += "/device_planned" if dp else ""
+            key += "/device_plan_reused" if dp == "reuse" else ("/device_planned" if dp else "")
             key += "/qkv_%s_x" % qkv if qkv else ""
             key += "_%dtok" % ntok if ntok else ""
-            if (name == args.workload and planned == head.planned and dp == head.devplan
-                    and not qkv):
+            if (name == args.workload and planned == head.planned and bool(dp) == head.devplan
+                    and (dp == "reuse") == head.reuse and not qkv):
                 continue
-            r = Runner(name, "fused", planned, qkv=qkv, n_tokens=ntok, devplan=dp)
+            r = Runner(name, "fused", planned, qkv=qkv, n_tokens=ntok, devplan=bool(dp),
+                       reuse=dp == "reuse")
             extra[key] = r.record(steps, warm)
             r.close()
             print("[bench] %s: %.1f us per step, %.3f of 8 TB/s" % (

@@ -36,6 +36,7 @@ EXPORTS = (
     "lora_page_table_build", "lora_pool_export_entry", "lora_pool_export_scales",
     "lora_pool_read_pages", "lora_bgmv_shrink", "lora_bgmv_expand",
     "lora_bgmv_apply", "lora_bgmv_planned_workspace_size", "lora_bgmv_apply_planned",
+    "lora_dplan_create", "lora_dplan_destroy", "lora_dplan_build", "lora_dplan_apply",
     "lora_plan_create", "lora_plan_destroy", "lora_plan_build",
     "lora_plan_get_stats", "lora_plan_export", "lora_plan_prepare", "lora_workspace_size",
     "lora_sgmv_shrink", "lora_sgmv_expand", "lora_apply", "lora_apply_noalloc", "lora_debug_resolve",
@@ -117,6 +118,10 @@ def _load() -> ctypes.CDLL:
         "lora_bgmv_planned_workspace_size": [V, I32, ctypes.POINTER(Io), I32,
                                              ctypes.POINTER(ctypes.c_size_t)],
         "lora_bgmv_apply_planned": [V, I32, ctypes.POINTER(Io), V, I32, I32, V, ctypes.c_size_t, V],
+        "lora_dplan_create": [V, I32, I32, ctypes.POINTER(Io), ctypes.POINTER(V)],
+        "lora_dplan_destroy": [V],
+        "lora_dplan_build": [V, I32, ctypes.POINTER(Io), V, I32, V],
+        "lora_dplan_apply": [V, V, I32, ctypes.POINTER(Io), I32, V],
         "lora_plan_create": [V, I32, ctypes.POINTER(V)],
         "lora_plan_destroy": [V],
         "lora_plan_build": [V, V, I32, I32, V],
@@ -441,6 +446,37 @@ def lora_bgmv_apply_planned(pool: int, ios: Sequence[Tuple[int, object, object]]
                                         wp, wb, _stream(stream)), "lora_bgmv_apply_planned")
 
 
+def lora_dplan_create(pool: int, max_tokens: int, slices: Sequence[int]) -> int:
+    """A device plan for up to max_tokens tokens over slices of these shapes."""
+    arr = _slice_ios(slices)
+    h = ctypes.c_void_p()
+    _check(_lib.lora_dplan_create(pool, int(max_tokens), len(slices), arr, ctypes.byref(h)),
+           "lora_dplan_create")
+    return h.value
+
+
+def lora_dplan_destroy(dplan: int):
+    _check(_lib.lora_dplan_destroy(dplan), "lora_dplan_destroy")
+
+
+def lora_dplan_build(dplan: int, slices: Sequence[int], ids, stream=None):
+    """Group the device ids by adapter (residency of `slices`) into the plan."""
+    _check_ids(ids)
+    arr = _slice_ios(slices)
+    _check(_lib.lora_dplan_build(dplan, len(slices), arr, _dev_ptr(ids), int(ids.shape[0]),
+                                 _stream(stream)), "lora_dplan_build")
+
+
+def lora_dplan_apply(pool: int, dplan: int, ios: Sequence[Tuple[int, object, object]], n: int,
+                     y_dtype: int, stream=None):
+    """The plan's MFMA launches on ios (slices of the plan's shapes); n: the
+    tokens of the last build (checks the x and y buffers)."""
+    _check_io(pool, ios, int(n), y_dtype)
+    arr = _ios(ios)
+    _check(_lib.lora_dplan_apply(pool, dplan, len(ios), arr, y_dtype, _stream(stream)),
+           "lora_dplan_apply")
+
+
 # ----------------------------------------------------------------------------
 # SGMV
 # ----------------------------------------------------------------------------
@@ -597,6 +633,14 @@ def prepare_bgmv_apply_planned(pool: int, ios: Sequence[Tuple[int, object, objec
     return PreparedCall(_lib.lora_bgmv_apply_planned, (pool, len(ios), arr, _dev_ptr(ids),
                                                        int(ids.shape[0]), y_dtype, wp, wb),
                         "lora_bgmv_apply_planned", (ios, ids, arr, workspace))
+
+
+def prepare_dplan_apply(pool: int, dplan: int, ios: Sequence[Tuple[int, object, object]], n: int,
+                        y_dtype: int) -> PreparedCall:
+    _check_io(pool, ios, int(n), y_dtype)
+    arr = _ios(ios)
+    return PreparedCall(_lib.lora_dplan_apply, (pool, dplan, len(ios), arr, y_dtype),
+                        "lora_dplan_apply", (ios, arr))
 
 
 def prepare_apply(pool: int, plan: int, ios: Sequence[Tuple[int, object, object]], y_dtype: int,

@@ -5,6 +5,7 @@
 // caller.
 #include <algorithm>
 #include <cstring>
+#include <new>
 
 #include "devplan.h"
 #include "runtime.h"
@@ -157,6 +158,22 @@ lora_status devplan_shape(const lora_pool* p, const IoSet& ios, int32_t n, DevPl
 
 }  // namespace
 
+// A device plan kept between calls: built from device ids by lora_dplan_build,
+// applied by lora_dplan_apply to any launch whose slices have the shapes it
+// was created for (the layers of a model whose LoRA calls share one decode
+// step's ids).  Owns its device workspace.
+struct lora_dplan {
+  lora_pool* pool = nullptr;
+  int32_t max_tokens = 0;
+  int32_t n_io = 0;
+  int32_t d_in[LORA_MAX_IO] = {}, d_out[LORA_MAX_IO] = {};
+  lora::DevPlanShape sh{};   // shape of the last build (slices, token count)
+  lora::DevPlanWs w{};       // workspace layout for max_tokens
+  char* ws = nullptr;
+  bool built = false;
+  uint64_t generation = ~0ull;  // pool residency the plan was built against
+};
+
 #define LORA_TRY(expr)          \
   do {                          \
     lora_status _s = (expr);    \
@@ -254,6 +271,107 @@ lora_status lora_bgmv_apply_planned(lora_pool* p, int32_t n_io, const lora_io* i
   return hip_status(launch_devplan_apply(p->types(y_dtype), p->view(), ios, ids, sh, w,
                                          reinterpret_cast<char*>(ws), (hipStream_t)stream),
                     "bgmv_apply_planned");
+}
+
+lora_status lora_dplan_create(lora_pool* p, int32_t max_tokens, int32_t n_io, const lora_io* io,
+                              lora_dplan** out) {
+  clear_error();
+  if (!p || !out) return fail(LORA_E_ARG, "null argument");
+  *out = nullptr;
+  if (max_tokens <= 0) return fail(LORA_E_ARG, "max_tokens must be positive");
+  if (n_io < 1 || n_io > LORA_MAX_IO || !io) return fail(LORA_E_ARG, "n_io must be in [1, %d]", LORA_MAX_IO);
+  IoSet ios;
+  memset(&ios, 0, sizeof(ios));
+  ios.n_io = n_io;
+  for (int k = 0; k < n_io; ++k) {
+    LORA_TRY(check_slice(p, io[k].slice));
+    ios.io[k] = p->io(io[k].slice, nullptr, nullptr);
+  }
+  DevPlanShape sh;
+  DevPlanWs w;
+  LORA_TRY(devplan_shape(p, ios, max_tokens, sh, w));
+  lora_dplan* d = new (std::nothrow) lora_dplan();
+  if (!d) return fail(LORA_E_NOMEM, "out of host memory");
+  d->pool = p;
+  d->max_tokens = max_tokens;
+  d->n_io = n_io;
+  for (int k = 0; k < n_io; ++k) {
+    d->d_in[k] = ios.io[k].d_in;
+    d->d_out[k] = ios.io[k].d_out;
+  }
+  d->sh = sh;
+  d->w = w;
+  if (!p->host_only) {
+    const hipError_t e = hipMalloc((void**)&d->ws, w.bytes);
+    if (e != hipSuccess) {
+      delete d;
+      return fail(LORA_E_NOMEM, "device plan workspace of %zu bytes: %s", w.bytes, hipGetErrorString(e));
+    }
+  }
+  *out = d;
+  return LORA_OK;
+}
+
+lora_status lora_dplan_destroy(lora_dplan* d) {
+  clear_error();
+  if (!d) return LORA_OK;
+  if (d->ws) {
+    (void)hipDeviceSynchronize();  // launches may still read the plan
+    (void)hipFree(d->ws);
+  }
+  delete d;
+  return LORA_OK;
+}
+
+lora_status lora_dplan_build(lora_dplan* d, int32_t n_io, const lora_io* io, const int32_t* ids,
+                             int32_t n, void* stream) {
+  clear_error();
+  if (!d) return fail(LORA_E_ARG, "null device plan");
+  lora_pool* p = d->pool;
+  if (n < 0 || n > d->max_tokens) return fail(LORA_E_ARG, "n %d outside [0, %d]", n, d->max_tokens);
+  if (n_io != d->n_io || !io) return fail(LORA_E_ARG, "%d slices, the plan was created for %d", n_io, d->n_io);
+  DevPlanShape sh = d->sh;
+  for (int k = 0; k < n_io; ++k) {
+    LORA_TRY(check_slice(p, io[k].slice));
+    if (p->d_in[(size_t)io[k].slice] != d->d_in[k] || p->d_out[(size_t)io[k].slice] != d->d_out[k])
+      return fail(LORA_E_ARG, "io %d: slice %d does not have the shape the plan was created for", k, io[k].slice);
+    sh.slice[k] = io[k].slice;
+  }
+  if (n > 0 && !ids) return fail(LORA_E_ARG, "null ids");
+  LORA_TRY(check_pool(p));
+  sh.n = n;
+  d->built = false;
+  if (n > 0) {
+    const hipError_t e = launch_devplan(p->view(), ids, sh, d->w, d->ws, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LORA_E_HIP, "dplan_build launch: %s", hipGetErrorString(e));
+  }
+  d->sh = sh;
+  d->built = true;
+  d->generation = p->generation;
+  return LORA_OK;
+}
+
+lora_status lora_dplan_apply(lora_pool* p, const lora_dplan* d, int32_t n_io, const lora_io* io,
+                             int32_t y_dtype, void* stream) {
+  clear_error();
+  if (!p || !d) return fail(LORA_E_ARG, "null argument");
+  if (d->pool != p) return fail(LORA_E_ARG, "device plan belongs to another pool");
+  if (!d->built) return fail(LORA_E_STATE, "device plan not built");
+  if (d->generation != p->generation)
+    return fail(LORA_E_STATE, "residency changed since the device plan was built");
+  LORA_TRY(check_ydt(p, y_dtype));
+  IoSet ios;
+  LORA_TRY(build_ioset(p, n_io, io, ios));
+  if (n_io != d->n_io) return fail(LORA_E_ARG, "%d slices, the plan was created for %d", n_io, d->n_io);
+  for (int k = 0; k < n_io; ++k)
+    if (ios.io[k].d_in != d->d_in[k] || ios.io[k].d_out != d->d_out[k])
+      return fail(LORA_E_ARG, "io %d: slice %d does not have the shape the plan was created for", k,
+                  ios.io[k].slice);
+  if (d->sh.n == 0) return LORA_OK;
+  LORA_TRY(check_pool(p));
+  return hip_status(launch_devplan_mfma(p->types(y_dtype), p->view(), ios, d->sh, d->w, d->ws,
+                                        (hipStream_t)stream),
+                    "dplan_apply");
 }
 
 lora_status lora_sgmv_shrink(lora_pool* p, const lora_plan* pl, int32_t slice, const void* x,

@@ -139,8 +139,12 @@ inline DevPlanOut devplan_out(char* ws, const DevPlanWs& w) {
   return o;
 }
 
-// Plan (one workgroup) then the planned MFMA apply, all on stream s; ws holds
-// w.bytes bytes (defined in k_devplan.hip).
+// Launchers (k_devplan.hip), all on stream s; ws holds w.bytes bytes.  The
+// plan alone (one workgroup); the planned MFMA apply from a plan in ws; both.
+hipError_t launch_devplan(const PoolView& pv, const int32_t* ids, const DevPlanShape& sh,
+                          const DevPlanWs& w, char* ws, hipStream_t s);
+hipError_t launch_devplan_mfma(const Types& ty, const PoolView& pv, const IoSet& ios,
+                               const DevPlanShape& sh, const DevPlanWs& w, char* ws, hipStream_t s);
 hipError_t launch_devplan_apply(const Types& ty, const PoolView& pv, const IoSet& ios,
                                 const int32_t* ids, const DevPlanShape& sh, const DevPlanWs& w,
                                 char* ws, hipStream_t s);

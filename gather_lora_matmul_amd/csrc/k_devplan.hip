@@ -53,13 +53,15 @@ __global__ __launch_bounds__(kDpThreads) void k_devplan(PoolView pv, DevPlanShap
 
 }  // namespace
 
-hipError_t launch_devplan_apply(const Types& ty, const PoolView& pv, const IoSet& ios,
-                                const int32_t* ids, const DevPlanShape& sh, const DevPlanWs& w,
-                                char* ws, hipStream_t s) {
+hipError_t launch_devplan(const PoolView& pv, const int32_t* ids, const DevPlanShape& sh,
+                          const DevPlanWs& w, char* ws, hipStream_t s) {
+  hipLaunchKernelGGL(k_devplan, dim3(1), dim3(kDpThreads), 0, s, pv, sh, ids, devplan_out(ws, w));
+  return hipGetLastError();
+}
+
+hipError_t launch_devplan_mfma(const Types& ty, const PoolView& pv, const IoSet& ios,
+                               const DevPlanShape& sh, const DevPlanWs& w, char* ws, hipStream_t s) {
   const DevPlanOut o = devplan_out(ws, w);
-  hipLaunchKernelGGL(k_devplan, dim3(1), dim3(kDpThreads), 0, s, pv, sh, ids, o);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   PlanView pl;
   pl.items = o.items;
   pl.perm = o.perm;
@@ -76,6 +78,14 @@ hipError_t launch_devplan_apply(const Types& ty, const PoolView& pv, const IoSet
   pl.n_mfma = sh.n;
   pl.G = sh.G;
   return launch_apply(ty, pv, pl, ios, s);
+}
+
+hipError_t launch_devplan_apply(const Types& ty, const PoolView& pv, const IoSet& ios,
+                                const int32_t* ids, const DevPlanShape& sh, const DevPlanWs& w,
+                                char* ws, hipStream_t s) {
+  const hipError_t e = launch_devplan(pv, ids, sh, w, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_devplan_mfma(ty, pv, ios, sh, w, ws, s);
 }
 
 }  // namespace lora

@@ -68,6 +68,7 @@ typedef enum {
 
 typedef struct lora_pool lora_pool; /* opaque, library-owned */
 typedef struct lora_plan lora_plan; /* opaque, library-owned */
+typedef struct lora_dplan lora_dplan; /* opaque, library-owned: a plan built on the device */
 
 #define LORA_MAX_SLICES 16
 #define LORA_MAX_RANK 128
@@ -374,6 +375,34 @@ lora_status lora_bgmv_planned_workspace_size(lora_pool* pool, int32_t n_io,
 lora_status lora_bgmv_apply_planned(lora_pool* pool, int32_t n_io, const lora_io* io_host,
                                     const int32_t* ids_dev, int32_t n, int32_t y_dtype,
                                     void* workspace_dev, size_t ws_bytes, void* stream);
+
+/* A device plan kept between calls, for the layers of a model whose LoRA calls
+ * share one decode step's ids: built once per step from the ids on the device,
+ * applied to every launch whose slices have the shapes it was created for.
+ * lora_dplan_create: for up to max_tokens tokens over slices with the shapes
+ * (d_in, d_out) of io[k].slice, in this order; allocates the plan's device
+ * workspace (the same size as lora_bgmv_planned_workspace_size), so it may
+ * allocate and synchronise; refusals as for lora_bgmv_planned_workspace_size.
+ * lora_dplan_destroy waits for the device. */
+lora_status lora_dplan_create(lora_pool* pool, int32_t max_tokens, int32_t n_io,
+                              const lora_io* io_host, lora_dplan** out);
+lora_status lora_dplan_destroy(lora_dplan* dplan);
+/* The planning launch of lora_bgmv_apply_planned alone, on `stream`: groups
+ * the n (<= max_tokens) ids by adapter.  A token takes part when its adapter
+ * is resident in at least one slice of io (same shapes as at creation, else
+ * LORA_E_ARG).  Stream-ordered, no allocation, no wait. */
+lora_status lora_dplan_build(lora_dplan* dplan, int32_t n_io, const lora_io* io_host,
+                             const int32_t* ids_dev, int32_t n, void* stream);
+/* The MFMA launches of lora_bgmv_apply_planned from the last build, on
+ * `stream` (stream-ordered after that build), for slices with the plan's
+ * shapes in the plan's order (other layers' slices included: LORA_E_ARG
+ * otherwise).  An adapter not resident in a slice leaves that slice's rows
+ * untouched.  LORA_E_STATE before a build or after any residency change of
+ * the pool since it.  Calls reading one plan may run one after another; a
+ * build while earlier applies of the plan are in flight on another stream
+ * races with them. */
+lora_status lora_dplan_apply(lora_pool* pool, const lora_dplan* dplan, int32_t n_io,
+                             const lora_io* io_host, int32_t y_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Debug / verification of the page-table resolution done inside the kernels.

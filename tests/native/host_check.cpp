@@ -38,6 +38,10 @@ hipError_t launch_sgmv_expand(const Types&, const PoolView&, const PlanView&, co
 hipError_t launch_apply(const Types&, const PoolView&, const PlanView&, const IoSet&, hipStream_t) STUB()
 hipError_t launch_devplan_apply(const Types&, const PoolView&, const IoSet&, const int32_t*,
                                 const DevPlanShape&, const DevPlanWs&, char*, hipStream_t) STUB()
+hipError_t launch_devplan(const PoolView&, const int32_t*, const DevPlanShape&, const DevPlanWs&,
+                          char*, hipStream_t) STUB()
+hipError_t launch_devplan_mfma(const Types&, const PoolView&, const IoSet&, const DevPlanShape&,
+                               const DevPlanWs&, char*, hipStream_t) STUB()
 hipError_t launch_debug_decode(int, const void*, int64_t, float*, hipStream_t) STUB()
 hipError_t launch_debug_resolve(const PoolView&, const IoDesc&, int32_t, int, const int32_t*, int32_t,
                                 int64_t*, int64_t*, hipStream_t) STUB()

@@ -424,3 +424,38 @@ def test_device_planned_decode_arguments():
             assert e.value.status == -7, args
         finally:
             sp.close()
+
+
+def test_device_plan_handle_arguments():
+    # lora_dplan_*: created for slice shapes, built on slices of those shapes,
+    # applied only to launches of those shapes, never before a build, refused
+    # on host-only pools before anything runs
+    wl = W.make_workload(2)  # slices 4096x4096 and 4096x11008
+    sp = _host_pool(wl, adapters=[0, 1, 2])
+    try:
+        d = L.lora_dplan_create(sp.handle, 256, [0, 1])
+        lib = L.lib()
+        fake = 1 << 20  # never dereferenced
+        io01 = (L.Io * 2)(L.Io(0, 0, fake, fake), L.Io(1, 0, fake, fake))
+        io10 = (L.Io * 2)(L.Io(1, 0, fake, fake), L.Io(0, 0, fake, fake))
+        assert lib.lora_dplan_apply(sp.handle, d, 2, io01, L.LORA_BF16, None) == -5  # not built
+        assert "not built" in L.lora_last_error()
+        assert lib.lora_dplan_build(d, 2, io10, fake, 64, None) == -1  # shapes swapped
+        assert lib.lora_dplan_build(d, 2, io01, fake, 257, None) == -1  # past max_tokens
+        assert lib.lora_dplan_build(d, 1, io01, fake, 64, None) == -1   # slice count
+        st = lib.lora_dplan_build(d, 2, io01, fake, 64, None)
+        assert st == -5 and "host-only" in L.lora_last_error()
+        assert lib.lora_dplan_build(d, 2, io01, None, 0, None) == -5
+        L.lora_dplan_destroy(d)
+        with pytest.raises(L.LoraError) as e:
+            L.lora_dplan_create(sp.handle, 1025, [0])
+        assert e.value.status == -1
+    finally:
+        sp.close()
+    sp = _host_pool(W.small_workload("f32", 256, 256, [4, 8], 256))
+    try:
+        with pytest.raises(L.LoraError) as e:
+            L.lora_dplan_create(sp.handle, 8, [0])
+        assert e.value.status == -7
+    finally:
+        sp.close()

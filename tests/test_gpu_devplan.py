@@ -187,3 +187,40 @@ def test_devplan_workspace_checks():
         L.lora_bgmv_planned_workspace_size(sp.handle, [0], 1025)
     torch.cuda.synchronize()
     assert np.all(y.cpu().view(torch.int16).numpy() == 0)  # nothing launched
+
+
+def test_dplan_built_once_applied_to_other_layers():
+    """One device plan built from a batch's ids on slices 0 and 1, applied to
+    slices 0, 1 and to slices 2, 3 (another layer of the same shapes): every
+    row of all four slices against the oracle, the bits equal to the one-shot
+    lora_bgmv_apply_planned; a residency change makes the plan stale."""
+    wl = W.small_workload("bf16", 1024, 1000, [8, 40, 16, 64, 24], 1024, n_slices=4, seed=23)
+    sp = SyntheticPool(wl)
+    d = L.lora_dplan_create(sp.handle, 300, [0, 1])
+    try:
+        rng = np.random.default_rng(9)
+        ids = rng.integers(-1, 5, 300).astype(np.int32)
+        ids[:120] = 2
+        log("[case] device plan built once, applied to two layers, 300 tokens")
+        b = W.custom_batch(wl, ids, zero_y0=False)
+        idt = ids_tensor(ids)
+        xs = {s: to_device(b.x[s], "bf16") for s in range(4)}
+        ys = {s: Guarded(b.y0[s], "bf16") for s in range(4)}
+        L.lora_dplan_build(d, [0, 1], idt)
+        L.lora_dplan_apply(sp.handle, d, [(0, xs[0], ys[0].view), (1, xs[1], ys[1].view)], 300, L.LORA_BF16)
+        L.lora_dplan_apply(sp.handle, d, [(2, xs[2], ys[2].view), (3, xs[3], ys[3].view)], 300, L.LORA_BF16)
+        torch.cuda.synchronize()
+        got = {s: ys[s].host() for s in range(4)}
+        check_all(wl, b, got, {}, [0, 1, 2, 3], "bf16", "dplan layers")
+        one, _ = run_planned(sp, b, [2, 3], "bf16")
+        for s in (2, 3):
+            assert got[s].tobytes() == one[s].tobytes(), "slice %d differs from the one-shot call" % s
+        L.lora_pool_evict(sp.handle, 4, 3)
+        L.lora_page_table_build(sp.handle)
+        with pytest.raises(L.LoraError) as ei:
+            L.lora_dplan_apply(sp.handle, d, [(2, xs[2], ys[2].view), (3, xs[3], ys[3].view)], 300,
+                               L.LORA_BF16)
+        assert ei.value.status == -5  # LORA_E_STATE
+    finally:
+        L.lora_dplan_destroy(d)
+        sp.close()
