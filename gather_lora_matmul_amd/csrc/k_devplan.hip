@@ -72,6 +72,7 @@ hipError_t launch_devplan_mfma(const Types& ty, const PoolView& pv, const IoSet&
   pl.c_ent = o.c_ent;
   pl.part = reinterpret_cast<float*>(ws + w.part);
   pl.n_tiles_dev = o.counts;
+  pl.pool = nullptr;
   // the host knows only a bound on the tiles; no short items
   pl.n_items = sh.n;
   pl.n_tokens = sh.n;

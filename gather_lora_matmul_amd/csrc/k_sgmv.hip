@@ -190,6 +190,9 @@ __global__ __launch_bounds__(kMT, 2) void k_apply_shrink_tiles(PoolView pv, Plan
   __shared__ __attribute__((aligned(16))) char bc[kBufB];
   const int L = logical_block(blockIdx.x, pl.G);
   const LdsBufs lb{misc, ba, bb, bc};
+  // the expand launch that follows claims its pool through this counter
+  if (pl.pool && blockIdx.x == 0 && threadIdx.x == 0)
+    reinterpret_cast<int*>(pl.part)[4 * (int64_t)pl.pool[2]] = 0;
   shrink_range<T>(pv, pl, [&](int j) -> const IoDesc& { return ios.io[j]; }, L, nullptr, 0, lb);
 }
 

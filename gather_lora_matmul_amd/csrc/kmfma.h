@@ -828,8 +828,8 @@ __device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView&
   uint16_t* Vl = reinterpret_cast<uint16_t*>(lb.b);
   float* Ds = reinterpret_cast<float*>(lb.c);
   const int ntl = plan_tiles(pl);
-  for_each_piece(pl.bs_expand, L, ntl, [&](int j) { return (io_of(j).d_out + 63) / 64; },
-                 [&](int j, int i, int c0, int c1, bool, bool) {
+  // chunks [c0, c1) of tile i in launch slice j
+  auto piece = [&](int j, int i, int c0, int c1) {
     const IoDesc io = io_of(j);
     const PlanItem item = pl.items[i];
     const DevEntry e = pv.entries[io.slice * pv.max_adapters + item.adapter];
@@ -885,7 +885,52 @@ __device__ __forceinline__ void expand_range(const PoolView& pv, const PlanView&
       }
     }
     lds_barrier();  // tokens and V are free (the y stores stay in flight)
-  });
+  };
+  // One loop and one call of `piece` (a second inlined copy of its body costs
+  // registers and spills): first the block's static range, then, in fused
+  // launches with a pool, claims of `batch` pool chunks until a claim starts
+  // past the pool's end (every block gets there; nothing waits).
+  const RangePos b = load_pos(pl.bs_expand, L + 1);
+  RangePos a = load_pos(pl.bs_expand, L);
+  bool pooled = false;
+  int g = 0, g1 = 0;  // pool chunks still to do in the current claim
+  __shared__ int claim;
+  for (;;) {
+    int j, i, c0, c1;
+    if (!pooled && pos_before(a.j, a.tile, a.k, b)) {
+      j = a.j;
+      i = a.tile;
+      c0 = a.k;
+      c1 = (a.j == b.j && a.tile == b.tile) ? b.k : (io_of(a.j).d_out + 63) / 64;
+      a.k = 0;
+      if (++a.tile == ntl) {
+        a.tile = 0;
+        ++a.j;
+      }
+    } else {
+      if (!kFused || !pl.pool) break;
+      pooled = true;
+      const RangePos p0 = load_pos(pl.bs_expand, pl.G);  // the pool's first tile
+      const int nch = (io_of(p0.j).d_out + 63) / 64;
+      if (g >= g1) {
+        const int pool_units = pl.pool[0], batch = pl.pool[1];
+        if (threadIdx.x == 0)
+          claim = atomicAdd(reinterpret_cast<int*>(pl.part) + 4 * (int64_t)pl.pool[2], batch);
+        __syncthreads();
+        g = claim;
+        __syncthreads();
+        if (g >= pool_units) break;
+        g1 = min(g + batch, pool_units);
+      }
+      const int t = g / nch;
+      j = p0.j;
+      i = p0.tile + t;
+      c0 = g - t * nch;
+      c1 = min(nch, c0 + (g1 - g));
+      g += c1 - c0;
+    }
+    piece(j, i, c0, c1);
+  }
 }
 
 }  // namespace lora

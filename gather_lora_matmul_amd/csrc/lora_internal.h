@@ -164,6 +164,10 @@ struct PlanView {
   // Plans built on the device: the tile count as the planner wrote it (the
   // host knows only a bound, in n_mfma); null for host-built plans.
   const int32_t* n_tiles_dev;
+  // Expand pool of a fused launch (null: none): {units, batch, float4 offset
+  // of the claim counter in part, 0}; the chunks from bs_expand[G] to the end
+  // of the sequence are claimed by blocks that finished their range.
+  const int32_t* pool;
   int32_t n_items;
   int32_t n_tokens;
   int32_t n_mfma;

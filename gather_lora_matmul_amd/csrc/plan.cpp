@@ -22,6 +22,16 @@ static_assert(sizeof(RangePos) == kPosInts * sizeof(int32_t), "device positions 
 
 namespace lora {
 
+// Fused launches of two or more slices leave about this fraction of the
+// expand weight (whole tiles at the end of the last slice) to a pool claimed
+// by the blocks that finish their ranges first: measured block durations
+// spread by 1.1-1.4x around the weights' prediction, which a static split
+// cannot absorb.  Only where the MFMA tiles hold at least kPoolMinFill tokens
+// on average: pieces of one- or two-token tiles are mostly set-up, and there
+// the claims cost more than the balance gains.
+constexpr double kExpandPoolFrac = 0.15;
+constexpr int kPoolMinFill = 8;
+
 std::vector<int32_t> layout_key(const IoSet& ios) {
   std::vector<int32_t> key;
   key.push_back(ios.n_io);
@@ -58,13 +68,14 @@ lora_status plan_prepare_layout(lora_plan* pl, const IoSet& ios, hipStream_t s) 
   lay->valid = false;
   LayoutHost h;
   if (!layout_host(pl->h_ws, pl->h_we, pl->h_tu, nst, nch, G, kPieceSetupShrink,
-                   kPieceSetupExpand, h))
+                   kPieceSetupExpand, h, false, J >= 2 && pl->mfma_tokens >= kPoolMinFill * pl->n_mfma ? kExpandPoolFrac : 0.0))
     return fail(LORA_E_ARG, "plan: partial-tile workspace exceeds 2^31 float4 units");
   const std::vector<int32_t>& buf = h.buf;
   const size_t bytes = sizeof(int32_t) * buf.size();
   if (pl->pool->host_only) {  // sizes only: nothing runs on a host-only pool
     lay->key = layout_key(ios);
     lay->part_units = h.part_units;
+    lay->pool = h.pool;
     lay->valid = true;
     lay->used = ++pl->layout_clock;
     return LORA_OK;
@@ -102,6 +113,8 @@ lora_status plan_prepare_layout(lora_plan* pl, const IoSet& ios, hipStream_t s) 
   lay->o_bs = h.o_bs;
   lay->o_be = h.o_be;
   lay->o_fl = h.o_fl;
+  lay->o_pool = h.o_pool;
+  lay->pool = h.pool;
   lay->o_off = h.o_off;
   lay->o_ent = h.o_ent;
   lay->valid = true;

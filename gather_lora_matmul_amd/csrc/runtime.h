@@ -163,8 +163,9 @@ struct PlanLayout {
   size_t cap = 0;             // bytes of each
   hipEvent_t ev = nullptr;    // the staging copy has been consumed
   bool ev_pending = false;
-  int64_t part_units = 0;     // float4 units of partial tiles
-  size_t o_bs = 0, o_be = 0, o_fl = 0, o_off = 0, o_ent = 0;  // int32 offsets
+  int64_t part_units = 0;     // float4 units of partial tiles (and the pool counter)
+  bool pool = false;          // the expand ranges leave a pool (fused launches of >= 2 slices)
+  size_t o_bs = 0, o_be = 0, o_fl = 0, o_pool = 0, o_off = 0, o_ent = 0;  // int32 offsets
 };
 constexpr int kPlanLayouts = 8;
 
@@ -219,6 +220,7 @@ struct lora_plan {
     v.c_ent = lay ? lay->d_buf + lay->o_ent : nullptr;
     v.part = reinterpret_cast<float*>(part);
     v.n_tiles_dev = nullptr;
+    v.pool = lay && lay->pool ? lay->d_buf + lay->o_pool : nullptr;
     v.n_items = n_items;
     v.n_tokens = n_tokens;
     v.n_mfma = n_mfma;

@@ -46,14 +46,23 @@ int main(int argc, char** argv) {
     }
     const int64_t ov_s = (trial % 2) ? 0 : 1 + rng() % 2000;
     const int64_t ov_e = (trial % 4 == 1) ? 0 : 1 + rng() % 3000;
+    // every third trial with two or more slices leaves an expand pool
+    const double pool_frac = (trial % 3 == 2) ? 0.05 + 0.05 * (rng() % 5) : 0.0;
     LayoutHost h;
-    if (!lora::layout_host(ws, we, tu, nst, nch, G, ov_s, ov_e, h)) {
+    if (!lora::layout_host(ws, we, tu, nst, nch, G, ov_s, ov_e, h, false, pool_frac)) {
       fail("layout_host refused", trial);
       continue;
     }
     const int32_t* fl = h.buf.data() + h.o_fl;
     const int32_t* coff = h.buf.data() + h.o_off;
     const int32_t* cent = h.buf.data() + h.o_ent;
+    const int32_t* pool = h.buf.data() + h.o_pool;
+    if (h.pool != (pool_frac > 0 && J >= 2)) fail("pool presence", trial);
+    // the pool: whole tiles at the end of the last slice
+    const int pool_t0 = h.pool ? T - pool[0] / nch[J - 1] : T;
+    if (h.pool && (pool[0] % nch[J - 1] != 0 || pool_t0 < 0 || pool_t0 >= T ||
+                   pool[1] < std::min(8, nch[J - 1]) || pool[1] > nch[J - 1]))
+      fail("pool shape", trial);
     for (int pass = 0; pass < 2; ++pass) {
       const int32_t* tab = h.buf.data() + (pass ? h.o_be : h.o_bs);
       const std::vector<int32_t>& n = pass ? nch : nst;
@@ -64,10 +73,17 @@ int main(int argc, char** argv) {
       for (int j = 0; j < J; ++j)
         for (int t = 0; t < T; ++t) cover[(size_t)j * T + t].assign(n[j], 0);
       const P a0 = at(tab, 0), aG = at(tab, G);
-      if (!(a0.j == 0 && a0.t == 0 && a0.k == 0) || !(aG.j == J && aG.t == 0 && aG.k == 0)) fail("ends", trial);
+      // the expand ranges end where the pool starts
+      const P end = (pass && h.pool) ? P{J - 1, pool_t0, 0} : P{J, 0, 0};
+      if (!(aG.j == end.j && aG.t == end.t && aG.k == end.k)) fail("ends", trial);
+      if (lt(P{0, 0, 0}, end) && !(a0.j == 0 && a0.t == 0 && a0.k == 0)) fail("start", trial);
+      if (pass && h.pool)  // the pool's chunks, each claimed once
+        for (int t = pool_t0; t < T; ++t)
+          for (int kk = 0; kk < nch[J - 1]; ++kk) cover[(size_t)(J - 1) * T + t][kk]++;
       double total = 0, wmax = 0;
       for (int j = 0; j < J; ++j)
-        for (int t = 0; t < T; ++t) total += (double)n[j] * w[t];
+        for (int t = 0; t < T; ++t)
+          if (lt(P{j, t, 0}, end)) total += (double)n[j] * w[t];
       for (int x : w) wmax = std::max(wmax, (double)x);
       for (int L = 0; L < G; ++L) {
         const P a = at(tab, L), b = at(tab, L + 1);
@@ -114,7 +130,7 @@ int main(int argc, char** argv) {
         if (ov == 0 && wsum > total / G + wmax + 1e-6) fail("imbalance", trial);
         max_cost = std::max(max_cost, cost);
       }
-      if (ov > 0 && (int64_t)J * T <= lora::kMaxPiecesOv) {
+      if (ov > 0 && (int64_t)J * T <= lora::kMaxPiecesOv && !(pass && h.pool)) {
         // the plain split (no set-up cost) under the same cost: never better
         std::vector<int32_t> plain((size_t)kPosInts * (G + 1));
         lora::balance_ranges(w, n, G, 0, plain.data());
@@ -150,7 +166,8 @@ int main(int argc, char** argv) {
           if (cent[c] != expect) fail("partial offsets not disjoint", trial);
           expect += tu[t];
         }
-    if (expect != h.part_units || (size_t)coff[J * (T + 1) - 1] != h.buf.size() - h.o_ent)
+    if (h.pool && pool[2] != expect) fail("pool counter offset", trial);
+    if (expect + (h.pool ? 1 : 0) != h.part_units || (size_t)coff[J * (T + 1) - 1] != h.buf.size() - h.o_ent)
       fail("partial units", trial);
   }
   printf("%d trials, %d failures\n", trials, bad);
